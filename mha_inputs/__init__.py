@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs for multi-head attention forward.
+
+This module is the only code shared by the oracle side and the GPU side. It draws
+random numbers and encodes them; it contains none of the attention arithmetic.
+
+Draw recipe (one reading, since the workloads only say "i.i.d. from seed"):
+  * ``numpy.random.Generator(PCG64)`` seeded from ``SeedSequence(seed).spawn(3)``,
+    one child stream each for Q, K and V, drawn in that order;
+  * values are drawn in float32 (normal: ``standard_normal * sigma``; uniform:
+    ``uniform(lo, hi)``), then, for bfloat16 workloads, encoded to bf16 by
+    round-to-nearest-even on the host;
+  * the identical encoded bytes go to the GPU and to the oracle, which decodes
+    them exactly.
+
+Arrays are contiguous ``[B, H, N, d]``.  bf16 tensors are returned as ``uint16``
+bit patterns, fp32 tensors as ``float32``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Tuple
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "f32_to_bf16_bits",
+    "draw",
+    "draw_qkv",
+]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Encode float32 values to bfloat16 bit patterns, round-to-nearest-even.
+
+    Non-finite inputs are not expected (the draws are finite).
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+@dataclass(frozen=True)
+class Dist:
+    """A value distribution: ``("normal", sigma)`` or ``("uniform", lo, hi)``."""
+
+    kind: str
+    a: float = 1.0
+    b: float = 0.0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str  # "f32" or "bf16"
+    causal: bool
+    seed: int
+    qk_dist: Dist = field(default_factory=lambda: Dist("normal", 1.0))
+    v_dist: Dist = field(default_factory=lambda: Dist("normal", 1.0))
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+    @property
+    def shape(self) -> Tuple[int, int, int, int]:
+        return (self.B, self.H, self.N, self.d)
+
+    def credited_flops(self) -> float:
+        """4*B*H*N^2*d, halved for the causal mask."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2.0 if self.causal else f
+
+
+# The five attention-forward workloads: shapes, dtypes, distributions, masks.
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("fp32_B1_H2_N128_d64", 1, 2, 128, 64, "f32", False, seed=1),
+        Workload("bf16_B4_H16_N1024_d64", 4, 16, 1024, 64, "bf16", False, seed=2),
+        Workload("bf16_B4_H32_N4096_d128_causal", 4, 32, 4096, 128, "bf16", True, seed=3),
+        Workload("bf16_B1_H32_N16384_d128_causal", 1, 32, 16384, 128, "bf16", True, seed=4),
+        Workload(
+            "bf16_B8_H16_N8192_d64_stress",
+            8, 16, 8192, 64, "bf16", False, seed=5,
+            qk_dist=Dist("normal", 3.0),
+            v_dist=Dist("uniform", -1.0, 1.0),
+        ),
+    ]
+}
+
+
+def _sample(rng: np.random.Generator, shape, dist: Dist) -> np.ndarray:
+    if dist.kind == "normal":
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        if dist.a != 1.0:
+            x *= np.float32(dist.a)
+        return x
+    if dist.kind == "uniform":
+        return rng.uniform(dist.a, dist.b, size=shape).astype(np.float32)
+    raise ValueError(f"unknown distribution {dist.kind!r}")
+
+
+def draw(shape, dtype: str, seed: int, qk_dist: Dist = Dist("normal", 1.0),
+         v_dist: Dist = Dist("normal", 1.0)) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Draw Q, K, V of ``shape`` (``[B,H,N,d]``) from ``seed``.
+
+    Returns float32 arrays for ``dtype == "f32"`` and uint16 bf16 bit patterns for
+    ``dtype == "bf16"``.
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    children = np.random.SeedSequence(seed).spawn(3)
+    out = []
+    for child, dist in zip(children, (qk_dist, qk_dist, v_dist)):
+        rng = np.random.Generator(np.random.PCG64(child))
+        x = _sample(rng, shape, dist)
+        out.append(f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x))
+    return out[0], out[1], out[2]
+
+
+def draw_qkv(w: Workload):
+    """Q, K, V for one of the named workloads."""
+    return draw(w.shape, w.dtype, w.seed, w.qk_dist, w.v_dist)

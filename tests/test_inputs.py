@@ -1,0 +1,45 @@
+"""Seeded synthetic inputs: determinism, the bf16 encoder and the distributions.  CPU only."""
+import numpy as np
+import torch
+
+import mha_inputs as mi
+
+
+def test_bf16_encoder_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.0e38, -3.0e38, 1e-40],
+                                 dtype=np.float32)])
+    # exact ties: 1 + 2^-8 rounds to 1 (even), 1 + 3*2^-8 rounds up to 1 + 2^-6
+    ours = mi.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert ours[-5] == 0x3F80 and ours[-4] == 0x3F82
+
+
+def test_draw_is_deterministic_and_seed_dependent():
+    a = mi.draw((1, 2, 8, 4), "bf16", 3)
+    b = mi.draw((1, 2, 8, 4), "bf16", 3)
+    c = mi.draw((1, 2, 8, 4), "bf16", 4)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    assert not np.array_equal(a[0], c[0])
+    assert not np.array_equal(a[0], a[1])  # Q and K come from different streams
+
+
+def test_distributions():
+    w = mi.Workload("t", 2, 4, 4096, 64, "bf16", False, seed=9,
+                    qk_dist=mi.Dist("normal", 3.0), v_dist=mi.Dist("uniform", -1.0, 1.0))
+    q, k, v = mi.draw_qkv(w)
+    dec = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    qf, vf = dec(q), dec(v)
+    assert abs(qf.std() - 3.0) < 0.02 and abs(qf.mean()) < 0.02
+    assert vf.min() >= -1.0 and vf.max() <= 1.0 and abs(vf.std() - 1 / np.sqrt(3)) < 0.01
+    f = mi.draw((1, 1, 64, 64), "f32", 1)[0]
+    assert f.dtype == np.float32 and f.shape == (1, 1, 64, 64)
+
+
+def test_named_workloads():
+    w = mi.WORKLOADS["bf16_B4_H32_N4096_d128_causal"]
+    assert (w.B, w.H, w.N, w.d, w.causal, w.dtype) == (4, 32, 4096, 128, True, "bf16")
+    assert w.credited_flops() == 4 * 4 * 32 * 4096 * 4096 * 128 / 2
+    assert abs(w.scale - 1 / np.sqrt(128)) < 1e-15
