@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Fused MHA forward benchmark on one MI355X.
+
+One step = one call of the fused forward (the whole hot path is one kernel launch)
+over the workload's inputs, already resident in HBM.  Prints ONE JSON line:
+TFLOP/s credited as 4*B*H*N^2*d (halved for causal) per second, the roofline of the
+kernel (MFMA-bound; achieved TFLOP/s from HIP events over the timed region on the
+launch stream, against the published dense bf16 peak), and the CPU oracle timed on a
+bounded sample of the same workload on the host cores.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused MHA fwd TFLOP/s + % of bf16 MFMA peak (B4 H32 N4096 d128 causal)"
+HEADLINE = "bf16_B4_H32_N4096_d128_causal"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense peaks (bf16 MFMA; fp32 matrix)
+HBM_GBS = 8000.0
+
+
+def _to_device(a, dtype, dev):
+    import numpy as np
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def time_gpu(w, steps, warmup, dev):
+    """Warm up, then time exactly `steps` launches bracketed by synchronisations."""
+    import torch
+
+    import head_attention_fa2_amd as mha
+    import mha_inputs
+
+    q, k, v = mha_inputs.draw_qkv(w)
+    tq, tk, tv = (_to_device(x, w.dtype, dev) for x in (q, k, v))
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        mha.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+    torch.cuda.synchronize(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        mha.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]      # ms, per launch
+    total_ms = ev[0].elapsed_time(ev[steps])
+    return dict(total_ms=total_ms, per_ms=per, wall_s=wall, inputs=(q, k, v), out=(o, lse))
+
+
+def parity_sample(w, inputs, out, n=24):
+    """Max abs error of sampled output rows against the CPU oracle."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    q, k, v = inputs
+    o, lse = out
+    rng = np.random.default_rng(123)
+    picks = [(int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.N))) for _ in range(n)]
+    picks += [(0, 0, 0), (w.B - 1, w.H - 1, w.N - 1)]
+    o_ref, l_ref = oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, picks=picks, dtype=w.dtype)
+    idx = torch.tensor(picks, dtype=torch.long, device=o.device)
+    og = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy()
+    lg = lse[idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy()
+    return dict(rows=len(picks), max_abs_dO=float(np.max(np.abs(og - o_ref))),
+                max_abs_dLSE=float(np.max(np.abs(lg - l_ref))))
+
+
+def cpu_baseline(w, inputs, seconds):
+    """The oracle as it stands on the host cores, over whole heads of the workload
+    until about `seconds` of work; reported in the metric's unit (credited TFLOP/s)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    q, k, v = inputs
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    heads_per_call = max(1, min(w.H, math.ceil(cores / max(1, math.ceil(w.N / 1024)))))
+    done_heads, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            b, h0 = divmod(done_heads, w.H)
+            if b >= w.B:
+                break
+            h1 = min(w.H, h0 + heads_per_call)
+            sl = (slice(b, b + 1), slice(h0, h1))
+            oracle.attention_forward(oracle.decode(q[sl], w.dtype), oracle.decode(k[sl], w.dtype),
+                                     oracle.decode(v[sl], w.dtype), causal=w.causal, scale=w.scale,
+                                     threads=cores)
+            done_heads += h1 - h0
+            if time.perf_counter() - t0 >= seconds:
+                break
+    el = time.perf_counter() - t0
+    flops = w.credited_flops() / (w.B * w.H) * done_heads
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done_heads} of {w.B * w.H} heads (b, h in order) of {w.name}, float64, "
+                      f"{el:.1f} s wall, numpy/OpenBLAS 1 thread per worker x {cores} workers"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also time every workload (lines on stderr)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the fused forward runs on a single MI355X; "
+              "multi-GPU runs are not part of this benchmark", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import head_attention_fa2_amd as mha
+    import mha_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mha.load()
+    dev = torch.device("cuda:0")
+    w = mha_inputs.WORKLOADS[args.workload]
+
+    r = time_gpu(w, args.steps, args.warmup, dev)
+    ms = r["total_ms"] / args.steps
+    flops = w.credited_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    avg_launch_ms = sum(r["per_ms"]) / len(r["per_ms"])
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "seed": w.seed, "pct_of_bf16_peak": round(100 * tflops / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": f"mha_fwd_kernel<{w.dtype},{w.d},{'causal' if w.causal else 'full'}>",
+                     "avg_launch_ms": round(avg_launch_ms, 5),
+                     "algorithmic_bytes": mha.mha_fwd_bytes(w.B, w.H, w.N, w.d, 1 if w.dtype == "bf16" else 0)},
+    }
+    if not args.no_parity:
+        line["parity"] = parity_sample(w, r["inputs"], r["out"])
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, r["inputs"], args.cpu_seconds)
+    del r
+    if args.sweep:
+        for name, ww in mha_inputs.WORKLOADS.items():
+            rr = time_gpu(ww, max(5, args.steps // 2), 3, dev)
+            m = rr["total_ms"] / max(5, args.steps // 2)
+            tf = ww.credited_flops() / (m * 1e-3) / 1e12
+            print(json.dumps({"workload": name, "ms": round(m, 5), "TFLOP/s": round(tf, 2),
+                              "pct_of_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2),
+                              "parity": parity_sample(ww, rr["inputs"], rr["out"], n=8)}),
+                  file=sys.stderr, flush=True)
+            del rr
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,138 @@
+"""Fused multi-head attention forward (FlashAttention-2 style) for AMD MI355X.
+
+The compute is entirely in ``libmha.so`` (hand-written HIP kernels for gfx950 behind
+the C ABI of ``include/mha.h``).  This module only marshals arguments: the functions
+``mha_fwd``, ``mha_fwd_validate``, ``mha_fwd_flops``, ``mha_fwd_bytes``,
+``mha_status_string`` and ``mha_version`` mirror the C entry points one to one, and
+:func:`fwd` is the PyTorch-facing convenience (device memory and the stream come from
+torch; nothing is computed in Python).  There is no fallback: if the library is not
+built or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "MHA_OK", "MHA_ERR_INVALID_ARG", "MHA_ERR_UNSUPPORTED", "MHA_ERR_HIP",
+    "MHA_DTYPE_F32", "MHA_DTYPE_BF16",
+    "library_path", "load", "mha_fwd", "mha_fwd_validate", "mha_fwd_flops",
+    "mha_fwd_bytes", "mha_status_string", "mha_version", "fwd", "MhaError",
+]
+
+MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_HIP = 0, 1, 2, 3
+MHA_DTYPE_F32, MHA_DTYPE_BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class MhaError(RuntimeError):
+    """A non-zero mha_status from the library."""
+
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(mha_status_string(status))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmha.so")
+
+
+def load() -> ctypes.CDLL:
+    """Load libmha.so (built in place by ``head_attention_fa2_amd.build``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with head_attention_fa2_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.mha_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.mha_fwd.restype = i
+    lib.mha_fwd_validate.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i]
+    lib.mha_fwd_validate.restype = i
+    lib.mha_fwd_flops.argtypes = [i, i, i, i, i]
+    lib.mha_fwd_flops.restype = ctypes.c_double
+    lib.mha_fwd_bytes.argtypes = [i, i, i, i, i]
+    lib.mha_fwd_bytes.restype = ctypes.c_double
+    lib.mha_status_string.argtypes = [i]
+    lib.mha_status_string.restype = ctypes.c_char_p
+    lib.mha_version.argtypes = []
+    lib.mha_version.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+# ---------------------------------------------------------------- C entry points, 1:1
+def mha_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int,
+            causal: int, scale: float, dtype: int, stream: int) -> int:
+    """Enqueue the fused forward on ``stream``; pointers are device addresses (ints)."""
+    return load().mha_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream)
+
+
+def mha_fwd_validate(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int,
+                     causal: int, scale: float, dtype: int) -> int:
+    return load().mha_fwd_validate(q, k, v, o, lse, B, H, N, d, causal, scale, dtype)
+
+
+def mha_fwd_flops(B: int, H: int, N: int, d: int, causal: int) -> float:
+    return load().mha_fwd_flops(B, H, N, d, causal)
+
+
+def mha_fwd_bytes(B: int, H: int, N: int, d: int, dtype: int) -> float:
+    return load().mha_fwd_bytes(B, H, N, d, dtype)
+
+
+def mha_status_string(status: int) -> str:
+    return load().mha_status_string(status).decode()
+
+
+def mha_version() -> str:
+    return load().mha_version().decode()
+
+
+# ---------------------------------------------------------------- torch convenience
+def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=None, lse=None,
+        stream=None) -> Tuple["object", "object"]:
+    """``O, LSE = fwd(q, k, v)`` for contiguous ``[B, H, N, d]`` CUDA tensors.
+
+    ``q, k, v``: float32 or bfloat16, same shape, dtype and device.  ``scale`` defaults
+    to 1/sqrt(d).  ``out`` / ``lse`` may be given to reuse buffers.  The kernel is
+    enqueued on ``stream`` (default: torch's current stream of q's device); the call
+    does not synchronise.
+    """
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or len({q.device, k.device, v.device}) != 1:
+        raise ValueError("q, k, v must be on the same GPU")
+    if q.dtype not in (torch.float32, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float32 or all bfloat16")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    dtype = MHA_DTYPE_BF16 if q.dtype == torch.bfloat16 else MHA_DTYPE_F32
+    with torch.cuda.device(q.device):
+        rc = mha_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, N, d, int(bool(causal)), float(scale), dtype, stream.cuda_stream)
+    if rc != MHA_OK:
+        raise MhaError(rc)
+    return out, lse

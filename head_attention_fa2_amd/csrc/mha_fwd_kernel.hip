@@ -1,0 +1,492 @@
+// Fused multi-head attention forward for gfx950 (AMD Instinct MI355X, CDNA4).
+//
+// Computes Algorithm 1 ("FlashAttention-2 forward") of "ML-Triton, A Multi-Level
+// Compilation and Language Extension to Triton GPU Programming", section 2.5: for each
+// (batch, head) the query rows are split into blocks; a block loads its Q rows once,
+// then streams K/V tiles, forms S = Q.K_j^T, updates the running row max m and row sum
+// l with the online softmax (the running-sum update of the "Long Softmax" puzzle in
+// "Triton学习", lorn3.bearblog.dev), accumulates O += P.V_j, and stores O / l and the
+// logsumexp m + ln l once at the end.  The work partition is the one section 2.5 takes
+// from FlashAttention-2: output rows are distributed over the wavefronts and every
+// wavefront reads all of K/V, so wavefronts never exchange partial results.
+//
+// Mapping onto CDNA4:
+//  * A workgroup of 4 wavefronts owns 128 query rows; each wavefront owns 32 rows.
+//  * Both contractions are v_mfma_f32_32x32x16_bf16 (fp32 inputs: v_mfma_f32_32x32x2_f32).
+//    The scores are formed transposed, S^T = K.Q^T, so that the 32 lanes of a column
+//    each own ONE query row: row max / row sum are in-lane reductions plus one
+//    exchange between lane n and lane n+32 (v_permlane32_swap).  Output likewise is
+//    O^T = V^T.P^T, so the per-row rescale and 1/l are in-lane multiplies.
+//  * K rows enter the first product in an order that swaps bits 2 and 3 of the row
+//    index inside each 32-row slab; the fp32 accumulator of S^T is then, register for
+//    register, the bf16 B operand P^T of the second product (8 consecutive keys per
+//    lane half), so P needs no cross-lane shuffle.
+//  * K/V tiles (64 keys) are copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+//    staging), double buffered: tile j+1 is in flight while tile j is consumed.
+//    LDS rows are XOR-swizzled in 16-byte chunks so that the MFMA operand reads of
+//    K (ds_read_b128) and of V^T (ds_read_b64_tr_b16, the gfx950 transposing LDS read)
+//    are free of bank conflicts.
+//  * exp is evaluated as exp2 with the scale folded into one FMA (log2(e) prescale, as
+//    the "Long Softmax" puzzle recommends).  The output rescale is lazy: the running max
+//    used as exponent offset is only moved when the true max exceeds it by more than
+//    2^8 in the exponent, so O and l are rarely rescaled; the final O / l and
+//    m + ln l are exact for whichever offset was used.
+//  * Causal: key tiles entirely above a wavefront's rows are skipped, only tiles that
+//    cross the diagonal (or the ragged end of the sequence) evaluate the mask, and
+//    heavy (late) query blocks are scheduled first.  Workgroup ids are remapped so that
+//    all query blocks of a head run on the same XCD and share its L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "mha_launch.h"
+#include "mha_layout.h"
+
+// copy_to_lds sets m0 itself right before each copy; nothing else in these kernels
+// reads m0, so declaring it clobbered is sound.
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace mha_impl {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr int kQW = 32;                  // query rows per wavefront
+constexpr int kBN = 64;                  // keys per K/V tile
+constexpr int kWaves = 4;                // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kBM = kQW * kWaves;        // query rows per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleLog2 = 8.0f;     // lazy-rescale threshold, in log2 units
+
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int N;          // sequence length
+  int nqb;        // query blocks per head
+  int total;      // workgroups
+  float qmul;     // sign(scale): Q is multiplied by it on load (1, -1 or 0)
+  float scale2;   // |scale| * log2(e), or log2(e) when scale == 0
+};
+
+// ---------------------------------------------------------------------------- LDS layout
+// Chunk swizzle, its inverse and the slab row permutation live in mha_layout.h.
+using mha_layout::lds_inv;
+using mha_layout::lds_off;
+using mha_layout::sigma;
+
+// Exchange with lane (l ^ 32): returns (own, partner) folded by max / sum.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  // a and b hold the same value on entry; afterwards lanes 0-31 have (own, partner's)
+  // and lanes 32-63 have (partner's, own) in (a, b).
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One 16-byte-per-lane copy HBM -> LDS (global_load_lds_dwordx4): lane l reads
+// sbase + voff and the data lands at LDS address lds + 16*l.  Issued as inline asm so
+// that the compiler does not track it: the only waits on these copies are the explicit
+// vmcnt waits of the tile pipeline, which order them against the LDS reads.
+__device__ __forceinline__ void copy_to_lds(const void* sbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wavefront are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Workgroup barrier for the LDS tile pipeline.  __syncthreads() would also wait for
+// every outstanding global load, including the prefetch of the next tile; here each
+// wavefront has already waited (vmcnt) for the loads of the tile about to be read, and
+// its LDS reads of the previous tile were consumed before it arrives, so only the
+// execution barrier is needed.  The empty asm statements keep the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------- kernel
+// Two workgroups (8 wavefronts) per CU when the double-buffered K/V tiles fit twice in
+// the 160 KiB of LDS; fp32 with d = 128 needs 128 KiB and runs one workgroup per CU.
+template <typename T, int D>
+constexpr int min_waves_per_eu() { return 2 * 2 * kBN * D * (int)sizeof(T) <= 80 * 1024 ? 2 : 1; }
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<T, D>())))
+void mha_fwd_kernel(Params p) {
+  constexpr bool kBF16 = sizeof(T) == 2;
+  constexpr int RB = D * (int)sizeof(T);        // bytes per K/V row
+  constexpr int R = RB / 16;                     // 16-byte chunks per row
+  constexpr int kTileBytes = kBN * RB;
+  constexpr int kLoads = kBN * R / kThreads;     // 16-byte loads per thread per tile
+  static_assert(kLoads * kThreads == kBN * R, "tile must split evenly");
+  constexpr int kDT = D / 32;                    // 32-wide output column blocks
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTileBytes];  // [buf][K,V]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;      // query column (and K row slot) within the wavefront
+  const int G = lane >> 5;      // lane half
+
+  // --- workgroup -> (head, query block).  Consecutive workgroup ids go to different
+  // XCDs, so renumber: the k-th workgroup dispatched to XCD x gets task x*T/8 + k, which
+  // keeps every head's query blocks on one XCD.  Causal: latest (heaviest) blocks first.
+  int id = blockIdx.x;
+  if ((p.total & 7) == 0) id = (id & 7) * (p.total >> 3) + (id >> 3);
+  const int bh = id / p.nqb;
+  int qb = id - bh * p.nqb;
+  if (CAUSAL) qb = p.nqb - 1 - qb;
+  const int N = p.N;
+  const int q0 = qb * kBM;
+  const int qw = q0 + wave * kQW;               // first query row of this wavefront
+  const int qrow = qw + n;                      // the query row this lane owns
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const T* __restrict__ Q = (const T*)p.q + head;
+  const char* Kbase = (const char*)((const T*)p.k + head);
+  const char* Vbase = (const char*)((const T*)p.v + head);
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+
+  // --- tile loader: thread (wave, lane) copies kLoads 16-byte chunks of K and of V.
+  // Load j of a thread fills LDS bytes [(j*kWaves + wave)*1024, +1024); the swizzle is
+  // periodic in the row index, so the global row of load j is row0 + j*kRowStep and
+  // its chunk is the same for every j.
+  constexpr int kRowStep = 1024 * kWaves / RB;
+  int ld_row[kLoads], ld_chunk[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    if (mha_layout::loader_periodic<R>() && j > 0) {
+      ld_row[j] = ld_row[0] + j * kRowStep;
+      ld_chunk[j] = ld_chunk[0];
+    } else {
+      lds_inv<R>((j * kWaves + wave) * 64 + lane, ld_row[j], ld_chunk[j]);
+    }
+  }
+  const int ld_row0 = ld_row[0];
+  const unsigned ld_off0 = (unsigned)(ld_row0 * RB + ld_chunk[0] * 16);
+  auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
+    const int k0 = t * kBN;
+    const char* kg = Kbase + (size_t)k0 * RB;
+    const char* vg = Vbase + (size_t)k0 * RB;
+    char* lk = smem + buf * 2 * kTileBytes;
+    char* lv = lk + kTileBytes;
+    if (k0 + kBN <= N) {
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const unsigned off = mha_layout::loader_periodic<R>()
+                                 ? ld_off0 + (unsigned)(j * kRowStep * RB)
+                                 : (unsigned)(ld_row[j] * RB + ld_chunk[j] * 16);
+        const int dst = (j * kWaves + wave) * 1024;
+        copy_to_lds(kg, off, lds_addr(lk + dst));
+        copy_to_lds(vg, off, lds_addr(lv + dst));
+      }
+    } else {
+      // ragged last tile: rows past the end re-read row N-1 (finite, masked later)
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        const int row = min(k0 + ld_row[j], N - 1) - k0;
+        const unsigned off = (unsigned)(row * RB + ld_chunk[j] * 16);
+        const int dst = (j * kWaves + wave) * 1024;
+        copy_to_lds(kg, off, lds_addr(lk + dst));
+        copy_to_lds(vg, off, lds_addr(lv + dst));
+      }
+    }
+  };
+
+  // --- Q operand, kept in registers for the whole loop ("Load Q" once).
+  // bf16: lane (n, G) holds Q[qrow][16kc + 8G .. +7] for kc = 0..D/16-1.
+  // fp32: lane (n, G) holds Q[qrow][8j + 4G .. +3] for j = 0..D/8-1.
+  constexpr int kQF = kBF16 ? D / 16 : D / 8;
+  typedef typename std::conditional<kBF16, bf16x8_t, f32x4_t>::type qfrag_t;
+  qfrag_t qf[kQF];
+  {
+    const bool valid = qrow < N;
+    const T* qr = Q + (size_t)(valid ? qrow : 0) * D;
+#pragma unroll
+    for (int j = 0; j < kQF; ++j) {
+      const int col = kBF16 ? 16 * j + 8 * G : 8 * j + 4 * G;
+      qf[j] = *(const qfrag_t*)(qr + col);
+      if (!valid) qf[j] = qfrag_t{};
+      // scaled logit = scale * q.k = |scale| * (sign(scale) q).k; multiplying by 1, -1
+      // or 0 is exact, so the row max below is always taken on the logit's own order.
+#pragma unroll
+      for (int e = 0; e < (int)(sizeof(qfrag_t) / sizeof(T)); ++e) qf[j][e] = (T)((float)qf[j][e] * p.qmul);
+    }
+  }
+
+  // --- per-lane LDS offsets of the MFMA operands (constant over tiles).
+  // K (A operand of S^T): lane (n, G) reads key row sigma(n) (+32 per slab), chunk
+  // 2kc + G.  Same chunk rule for both element types (8 bf16 or 4 fp32 per chunk).
+  constexpr int kKF = kQF;
+  int offK[kKF];
+#pragma unroll
+  for (int j = 0; j < kKF; ++j) offK[j] = mha_layout::k_operand_off<R>(lane, j);
+  // V^T (A operand of O^T, bf16): ds_read_b64_tr_b16 gathers, in each 16-lane group, a
+  // 4-key x 16-column block; source lane s supplies key (s >> 2) and the 4-column group
+  // chosen so that output lane m ends up with column sigma(m).
+  int offV[kBF16 ? kDT : 1][2];
+  if constexpr (kBF16) {
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) offV[dt][h] = mha_layout::v_operand_off<R>(lane, dt, h);
+  }
+
+  // --- running state: this lane's query row.
+  f32x16_t acc[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) acc[dt] = f32x16_t{};
+  float m_run = -__builtin_inff();   // exponent offset in raw score units
+  float l_run = 0.f;                 // this lane's share of the row sum
+  const float c2 = p.scale2;
+
+  auto compute_tile = [&](const char* lk, const char* lv, int k0, bool masked) __attribute__((always_inline)) {
+    // S^T = K_j . Q^T : two 32-key slabs, accumulated in alternation so consecutive
+    // MFMAs are independent; K operands are read two steps ahead.
+    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+    if constexpr (kBF16) {
+      constexpr int KC = D / 16;
+      bf16x8_t kf[KC][2];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) kf[kc][ks] = *(const bf16x8_t*)(lk + offK[kc] + ks * 32 * RB);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc][ks], qf[kc], s[ks], 0, 0, 0);
+      // schedule: 4 reads, then (2 MFMA, 2 reads) ..., then the last MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < KC - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < D / 8; ++j)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const f32x4_t kf = *(const f32x4_t*)(lk + offK[j] + ks * 32 * RB);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            s[ks] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[t], qf[j][t], s[ks], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Mask: accumulator register r of slab ks on lane half G is key
+    // k0 + 32ks + 16(r>>3) + 8G + (r&7).
+    if (masked) {
+      const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * ks + 16 * (r >> 3) + 8 * G + (r & 7);
+          if (key > lim) s[ks][r] = -__builtin_inff();
+        }
+    }
+    // Online softmax (running max / sum of the "Long Softmax" puzzle).
+    float mx = s[0][0];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ks][r]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const bool grow = (m_new - m_run) * c2 > kRescaleLog2;     // true on the first tile
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+      const float alpha = fast_exp2((m_run - m_use) * c2);    // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) acc[dt] *= alpha;
+      m_run = m_use;
+    }
+    const float mc = (m_run == -__builtin_inff() ? 0.f : m_run) * c2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(s[ks][r], c2, -mc));
+        s[ks][r] = e;
+        lsum += e;
+      }
+    l_run += lsum;
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T += V_j^T . P^T
+    if constexpr (kBF16) {
+      bf16x8_t pf[4];   // P^T operand for key chunks kc2 = 2ks + hh (16 keys each)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[2 * ks + hh][e] = (__bf16)s[ks][8 * hh + e];
+      bf16x8_t vf[4][kDT];
+#pragma unroll
+      for (int kc2 = 0; kc2 < 4; ++kc2)
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) {
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(lv + offV[dt][0] + kc2 * 16 * RB));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(lv + offV[dt][1] + kc2 * 16 * RB));
+          vf[kc2][dt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+      for (int kc2 = 0; kc2 < 4; ++kc2)
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc2][dt], pf[kc2], acc[dt], 0, 0, 0);
+      // schedule: 8 reads (4 operands), then (1 MFMA, 2 reads) ..., then the last MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * kDT - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    } else {
+      // fp32: two keys per MFMA.  B operand = P value in register u of slab ks (key
+      // 32ks + 16(u>>3) + 8G + (u&7)); A operand on lane (m, G) = V[that key][32dt + m].
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int key = 32 * ks + 16 * (u >> 3) + 8 * G + (u & 7);
+            const int col = dt * 32 + n;
+            const float vv = *(const float*)(lv + lds_off<R>(key, col >> 2) + (col & 3) * 4);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, s[ks][u], acc[dt], 0, 0, 0);
+          }
+    }
+  };
+
+  // --- main loop over K/V tiles, double buffered.  Unrolled by two so that the LDS
+  // buffer of each step is a compile-time address.
+  auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_tag)::value;
+    if (t + 1 < ntiles) {
+      issue_tile(t + 1, buf ^ 1);
+      wait_vmcnt<2 * kLoads>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    tile_barrier();
+    const int k0 = t * kBN;
+    if (!CAUSAL || k0 <= qw + kQW - 1) {               // else: every key is after every row
+      const bool need_mask = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > qw);
+      compute_tile(smem + buf * 2 * kTileBytes, smem + buf * 2 * kTileBytes + kTileBytes, k0, need_mask);
+    }
+    tile_barrier();
+  };
+  issue_tile(0, 0);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  // --- epilogue: O = acc / l, lse = m + ln l, each written once.
+  const float l = sum_halves(l_run);
+  const float inv = 1.0f / l;
+  if (qrow < N) {
+    T* orow = (T*)p.o + head + (size_t)qrow * D;
+    if constexpr (kBF16) {
+      // register r of block dt is column 32dt + 16(r>>3) + 8G + (r&7)
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          bf16x8_t ov;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(acc[dt][8 * hh + e] * inv);
+          *(bf16x8_t*)(orow + dt * 32 + 16 * hh + 8 * G) = ov;
+        }
+    } else {
+      // register r of block dt is column 32dt + 8(r>>2) + 4G + (r&3)
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4_t ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = acc[dt][4 * g + e] * inv;
+          *(f32x4_t*)(orow + dt * 32 + 8 * g + 4 * G) = ov;
+        }
+    }
+    if (G == 0) p.lse[(size_t)bh * N + qrow] = (m_run * c2 + __builtin_amdgcn_logf(l)) * kLn2;
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch(const Params& p, hipStream_t stream) {
+  hipLaunchKernelGGL((mha_fwd_kernel<T, D, CAUSAL>), dim3(p.total), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int fwd_query_block() { return kBM; }
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                      int N, int d, int causal, float scale, int is_bf16, hipStream_t stream) {
+  Params p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.N = N;
+  p.nqb = (N + kBM - 1) / kBM;
+  p.total = p.nqb * B * H;
+  p.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
+  p.scale2 = (scale != 0.f ? fabsf(scale) : 1.f) * kLog2e;
+  if (is_bf16) {
+    if (d == 64) return causal ? launch<__bf16, 64, true>(p, stream) : launch<__bf16, 64, false>(p, stream);
+    return causal ? launch<__bf16, 128, true>(p, stream) : launch<__bf16, 128, false>(p, stream);
+  }
+  if (d == 64) return causal ? launch<float, 64, true>(p, stream) : launch<float, 64, false>(p, stream);
+  return causal ? launch<float, 128, true>(p, stream) : launch<float, 128, false>(p, stream);
+}
+
+}  // namespace mha_impl

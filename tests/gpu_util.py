@@ -1,0 +1,32 @@
+"""Helpers for GPU tests: move seeded inputs to the device and outputs back."""
+import numpy as np
+import torch
+
+import head_attention_fa2_amd as mha
+import mha_inputs
+import oracle
+
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-3)}   # (O, LSE) max abs error
+
+
+def to_device(a: np.ndarray, dtype: str, dev="cuda:0"):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def run(q, k, v, dtype, causal, scale=None, stream=None):
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    o, lse = mha.fwd(tq, tk, tv, causal=causal, scale=scale, stream=stream)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_full(q, k, v, dtype, causal, scale):
+    return oracle.attention_forward(oracle.decode(q, dtype), oracle.decode(k, dtype),
+                                    oracle.decode(v, dtype), causal=causal, scale=scale)
+
+
+def draw(B, H, N, d, dtype, seed, qk_sigma=1.0, v_uniform=False):
+    return mha_inputs.draw((B, H, N, d), dtype, seed, mha_inputs.Dist("normal", qk_sigma),
+                           mha_inputs.Dist("uniform", -1.0, 1.0) if v_uniform else mha_inputs.Dist("normal", 1.0))

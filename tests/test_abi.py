@@ -1,0 +1,94 @@
+"""The C-ABI library: it loads, exports every entry point include/mha.h declares, and
+its host-side validation and accounting behave as documented.  No GPU work is
+launched: every mha_fwd call here is rejected on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_attention_fa2_amd as mha
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mha.h")
+
+OK, INVALID, UNSUPPORTED = mha.MHA_OK, mha.MHA_ERR_INVALID_ARG, mha.MHA_ERR_UNSUPPORTED
+BF16, F32 = mha.MHA_DTYPE_BF16, mha.MHA_DTYPE_F32
+P = 0x10000  # a 16-byte aligned fake address (never dereferenced by validation)
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mha_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mha.load()
+    names = declared_functions()
+    assert {"mha_fwd", "mha_fwd_validate", "mha_fwd_flops", "mha_fwd_bytes",
+            "mha_status_string", "mha_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+        assert hasattr(mha, name), name          # Python binding mirrors the C names
+
+
+def test_exported_symbols_are_c_linkage():
+    out = os.popen(f"nm -D --defined-only {mha.library_path()}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def v(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=64, causal=0, scale=0.125, dtype=BF16)
+    a.update(kw)
+    return mha.mha_fwd_validate(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                                a["d"], a["causal"], a["scale"], a["dtype"])
+
+
+def test_validate_accepts_good_arguments():
+    assert v() == OK
+    assert v(d=128, causal=1, dtype=F32) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INVALID), (dict(k=0), INVALID), (dict(v=0), INVALID), (dict(o=0), INVALID),
+    (dict(lse=0), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID),
+    (dict(causal=2), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(dtype=7), INVALID),
+    (dict(d=32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(q=P + 8), UNSUPPORTED), (dict(o=P + 4), UNSUPPORTED), (dict(lse=P + 2), UNSUPPORTED),
+    (dict(B=65536, H=65536, N=1 << 20), UNSUPPORTED),
+])
+def test_validate_rejects(kw, code):
+    assert v(**kw) == code
+
+
+def test_mha_fwd_rejects_before_launch():
+    # invalid arguments: mha_fwd returns the validation code and enqueues nothing
+    assert mha.mha_fwd(0, P, P, P, P, 1, 1, 16, 64, 0, 0.125, BF16, 0) == INVALID
+    assert mha.mha_fwd(P, P, P, P, P, 1, 1, 16, 80, 0, 0.125, BF16, 0) == UNSUPPORTED
+
+
+def test_flops_and_bytes():
+    assert mha.mha_fwd_flops(4, 32, 4096, 128, 1) == 4 * 4 * 32 * 4096 ** 2 * 128 / 2
+    assert mha.mha_fwd_flops(4, 16, 1024, 64, 0) == 4 * 4 * 16 * 1024 ** 2 * 64
+    assert mha.mha_fwd_bytes(4, 32, 4096, 128, BF16) == 4 * 4 * 32 * 4096 * 128 * 2 + 4 * 4 * 32 * 4096
+    assert mha.mha_fwd_bytes(1, 2, 128, 64, F32) == 4 * 2 * 128 * 64 * 4 + 4 * 2 * 128
+
+
+def test_status_strings():
+    for code in (OK, INVALID, UNSUPPORTED, mha.MHA_ERR_HIP):
+        s = mha.mha_status_string(code)
+        assert s.startswith(["MHA_OK", "MHA_ERR_INVALID_ARG", "MHA_ERR_UNSUPPORTED", "MHA_ERR_HIP"][code])
+    assert mha.mha_status_string(99) == "unknown mha_status"
+    assert mha.mha_version().startswith("mha-gfx950")
+
+
+def test_python_wrapper_checks_shapes_on_cpu():
+    import torch
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        mha.fwd(q, q, q)                    # CPU tensors are refused before any call
+    with pytest.raises(ValueError):
+        mha.fwd(q[0], q[0], q[0])           # wrong rank

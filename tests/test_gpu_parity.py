@@ -1,0 +1,179 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on identical
+seeded inputs.  Tolerances: fp32 inputs max|dO|, max|dLSE| <= 1e-4; bf16 inputs
+max|dO| <= 2e-2, max|dLSE| <= 1e-3."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import head_attention_fa2_amd as mha
+import mha_inputs
+import oracle
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+W = mha_inputs.WORKLOADS
+
+
+def _check(o, lse, o_ref, l_ref, dtype, what, magnitude=1.0):
+    tol_o, tol_l = gu.TOL[dtype]
+    tol_o, tol_l = tol_o * magnitude, tol_l * magnitude
+    eo = float(np.max(np.abs(o - o_ref)))
+    el = float(np.max(np.abs(lse - l_ref)))
+    print(f"{what}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), what
+    assert eo <= tol_o, f"{what}: O error {eo}"
+    assert el <= tol_l, f"{what}: LSE error {el}"
+
+
+# ---------------------------------------------------------------- element-wise, small
+# Each workload at a size the oracle evaluates whole in seconds: several 128-row query
+# blocks and 64-key tiles, with ragged tails where N is not a multiple of them.
+SMALL = [
+    ("fp32_B1_H2_N128_d64", dict(B=1, H=2, N=128)),                  # the full workload
+    ("bf16_B4_H16_N1024_d64", dict(B=4, H=16, N=1024)),              # the full workload
+    ("bf16_B4_H32_N4096_d128_causal", dict(B=2, H=3, N=1000)),
+    ("bf16_B1_H32_N16384_d128_causal", dict(B=1, H=2, N=2049)),
+    ("bf16_B8_H16_N8192_d64_stress", dict(B=2, H=2, N=1100)),
+]
+
+
+@pytest.mark.parametrize("name,shape", SMALL, ids=[s[0] for s in SMALL])
+def test_workload_elementwise(name, shape):
+    w = W[name]
+    q, k, v = mha_inputs.draw((shape["B"], shape["H"], shape["N"], w.d), w.dtype, w.seed,
+                              w.qk_dist, w.v_dist)
+    o, lse = gu.run(q, k, v, w.dtype, w.causal, w.scale)
+    o_ref, l_ref = gu.oracle_full(q, k, v, w.dtype, w.causal, w.scale)
+    _check(o, lse, o_ref, l_ref, w.dtype, f"{name} {shape}")
+
+
+# ---------------------------------------------------------------- full size, sampled rows
+def _picks(B, H, N, n=40, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, N - 1, N - 2, min(127, N - 1), min(128, N - 1), min(63, N - 1), min(64, N - 1), N // 2}
+    picks = [(int(rng.integers(B)), int(rng.integers(H)), int(i)) for i in sorted(rows)]
+    picks += [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(N))) for _ in range(n)]
+    picks += [(B - 1, H - 1, N - 1), (0, 0, 0)]
+    return picks
+
+
+@pytest.mark.parametrize("name", [n for n in W if n != "fp32_B1_H2_N128_d64"])
+def test_workload_full_size_sampled(name):
+    """The full workload in the launch configuration the benchmark times: every output
+    is checked for finiteness and for the convex-combination bound |O| <= max|V|;
+    sampled rows (block edges, first/last rows, random) are compared with the oracle."""
+    w = W[name]
+    q, k, v = mha_inputs.draw_qkv(w)
+    tq, tk, tv = (gu.to_device(x, w.dtype) for x in (q, k, v))
+    o, lse = mha.fwd(tq, tk, tv, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    vmax = float(tv.float().abs().amax())
+    assert float(o.float().abs().amax()) <= vmax * (1 + 2 ** -7) + 1e-6
+    picks = _picks(w.B, w.H, w.N)
+    o_ref, l_ref = oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, picks=picks,
+                                         dtype=w.dtype)
+    idx = torch.tensor(picks, dtype=torch.long, device=o.device)
+    og = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
+    lg = lse[idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy().astype(np.float64)
+    _check(og, lg, o_ref, l_ref, w.dtype, f"{name} full, {len(picks)} sampled rows")
+
+
+# ---------------------------------------------------------------- edge cases
+EDGE = []
+for dtype in ("bf16", "f32"):
+    for d in (64, 128):
+        for N in (1, 2, 63, 64, 65, 127, 129, 200, 257):
+            for causal in (False, True):
+                EDGE.append((1, 1, N, d, causal, dtype))
+EDGE += [(3, 5, 130, 64, True, "bf16"), (2, 1, 513, 128, False, "bf16"), (1, 3, 300, 64, True, "f32")]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,dtype", EDGE)
+def test_edge_shapes(B, H, N, d, causal, dtype):
+    q, k, v = gu.draw(B, H, N, d, dtype, seed=1000 + N + d, qk_sigma=1.5)
+    scale = 1 / math.sqrt(d)
+    o, lse = gu.run(q, k, v, dtype, causal, scale)
+    o_ref, l_ref = gu.oracle_full(q, k, v, dtype, causal, scale)
+    _check(o, lse, o_ref, l_ref, dtype, f"edge B{B} H{H} N{N} d{d} causal={causal} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scales_and_large_logits(dtype):
+    B, H, N, d = 1, 2, 300, 64
+    for sigma, scale in ((3.0, 0.125), (1.0, 1.0), (1.0, -0.3), (5.0, 0.5)):
+        q, k, v = gu.draw(B, H, N, d, dtype, seed=int(sigma * 10), qk_sigma=sigma)
+        for causal in (False, True):
+            o, lse = gu.run(q, k, v, dtype, causal, scale)
+            o_ref, l_ref = gu.oracle_full(q, k, v, dtype, causal, scale)
+            # fp32 logits of size |s| carry rounding of order |s| * 2^-24 * sqrt(d) from the
+            # float32 dot product itself; past |lse| ~ 16 the absolute bound scales with it.
+            mag = max(1.0, float(np.max(np.abs(l_ref))) / 16.0) if dtype == "f32" else 1.0
+            _check(o, lse, o_ref, l_ref, dtype, f"sigma={sigma} scale={scale} causal={causal}", mag)
+
+
+# ---------------------------------------------------------------- invariants on GPU output
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_invariants_on_gpu(dtype, d):
+    B, H, N = 1, 2, 333
+    tol_o, tol_l = gu.TOL[dtype]
+    q, k, v = gu.draw(B, H, N, d, dtype, seed=5)
+    ones = mha_inputs.f32_to_bf16_bits(np.ones_like(v, dtype=np.float32)) if dtype == "bf16" \
+        else np.ones(v.shape, dtype=np.float32)
+    zeros = np.zeros_like(q)
+    vf = oracle.decode(v, dtype)
+    for causal in (False, True):
+        o1, _ = gu.run(q, k, ones, dtype, causal)
+        assert np.max(np.abs(o1 - 1.0)) <= tol_o, "V = 1 gives O = 1"
+        oz, lz = gu.run(zeros, k, v, dtype, causal)
+        cnt = np.arange(1, N + 1, dtype=np.float64)
+        mean = np.cumsum(vf, axis=2) / cnt[None, None, :, None] if causal else \
+            np.broadcast_to(vf.mean(axis=2, keepdims=True), vf.shape)
+        lz_ref = np.log(cnt)[None, None] if causal else np.full(lz.shape, math.log(N))
+        assert np.max(np.abs(oz - mean)) <= tol_o, "Q = 0 gives the mean of visible V"
+        assert np.max(np.abs(lz - lz_ref)) <= tol_l, "Q = 0 gives lse = ln(#visible)"
+    perm = np.random.default_rng(3).permutation(N)
+    o, l = gu.run(q, k, v, dtype, False)
+    op, lp = gu.run(q, k[:, :, perm].copy(), v[:, :, perm].copy(), dtype, False)
+    assert np.max(np.abs(op - o)) <= tol_o and np.max(np.abs(lp - l)) <= tol_l, "key permutation"
+
+
+# ---------------------------------------------------------------- determinism, streams, errors
+def test_bitwise_repeatable_and_stream():
+    w = W["bf16_B4_H32_N4096_d128_causal"]
+    q, k, v = gu.draw(2, 4, 1500, 128, "bf16", seed=11)
+    tq, tk, tv = (gu.to_device(x, "bf16") for x in (q, k, v))
+    o1, l1 = mha.fwd(tq, tk, tv, causal=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = mha.fwd(tq, tk, tv, causal=True)
+    o3, l3 = mha.fwd(tq, tk, tv, causal=True, stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)) and torch.equal(l1, l3)
+    assert w.d == 128
+
+
+def test_out_buffers_fully_overwritten():
+    q, k, v = gu.draw(1, 2, 130, 64, "bf16", seed=12)
+    tq, tk, tv = (gu.to_device(x, "bf16") for x in (q, k, v))
+    out = torch.full_like(tq, float("nan"))
+    lse = torch.full((1, 2, 130), float("nan"), device=tq.device)
+    mha.fwd(tq, tk, tv, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+
+
+def test_errors_raise():
+    q = torch.zeros(1, 1, 16, 96, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(mha.MhaError) as e:
+        mha.fwd(q, q, q)
+    assert e.value.status == mha.MHA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        mha.fwd(q.half(), q.half(), q.half())
+    with pytest.raises(ValueError):
+        mha.fwd(q, q.float(), q)
