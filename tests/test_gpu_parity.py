@@ -149,6 +149,7 @@ def test_bitwise_repeatable_and_stream():
     tq, tk, tv = (gu.to_device(x, "bf16") for x in (q, k, v))
     o1, l1 = mha.fwd(tq, tk, tv, causal=True)
     s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())      # inputs were written on the current stream
     with torch.cuda.stream(s):
         o2, l2 = mha.fwd(tq, tk, tv, causal=True)
     o3, l3 = mha.fwd(tq, tk, tv, causal=True, stream=s)
