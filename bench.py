@@ -13,6 +13,7 @@ bounded sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -26,6 +27,32 @@ METRIC = "fused MHA fwd TFLOP/s + % of bf16 MFMA peak (B4 H32 N4096 d128 causal)
 HEADLINE = "bf16_B4_H32_N4096_d128_causal"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense peaks (bf16 MFMA; fp32 matrix)
 HBM_GBS = 8000.0
+
+
+KERNEL_SOURCES = ("mha_fwd_kernel.hip", "mha_layout.h", "mha_launch.h")
+
+
+def kernel_source_sha256() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "head_attention_fa2_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 (FETCH_SIZE, WRITE_SIZE, each scaled
+    by the same counter's reading for a plain copy of known size), or None when no
+    measurement exists for the kernel source as it is now."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path, encoding="utf-8") as fh:
+            entry = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return entry["traffic_bytes"]
 
 
 def _to_device(a, dtype, dev):
@@ -127,6 +154,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time every workload (lines on stderr)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 5 device-to-device copies of BYTES bytes (to scale HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the fused forward runs on a single MI355X; "
@@ -143,6 +172,16 @@ def main():
         sys.exit(1)
     mha.load()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        # A plain copy of known size: FETCH_SIZE should read and WRITE_SIZE should
+        # write exactly BYTES per launch; the ratio calibrates the counters.
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_calibration_bytes": args.copy_calibration, "launches": 5}))
+        return
     w = mha_inputs.WORKLOADS[args.workload]
 
     r = time_gpu(w, args.steps, args.warmup, dev)
@@ -168,7 +207,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "seed": w.seed, "pct_of_bf16_peak": round(100 * tflops / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": recorded_traffic(w.name),
                      "kernel": f"mha_fwd_kernel<{w.dtype},{w.d},{'causal' if w.causal else 'full'}>",
                      "avg_launch_ms": round(avg_launch_ms, 5),
                      "algorithmic_bytes": mha.mha_fwd_bytes(w.B, w.H, w.N, w.d, 1 if w.dtype == "bf16" else 0)},

@@ -19,6 +19,8 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
+    # the LDS copies set m0 in inline asm right before use; nothing else reads m0
+    "-Wno-inline-asm",
 ]
 
 

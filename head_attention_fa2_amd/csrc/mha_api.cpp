@@ -21,7 +21,7 @@ mha_status validate(const void* q, const void* k, const void* v, const void* o, 
   if (d != 64 && d != 128) return MHA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return MHA_ERR_UNSUPPORTED;
-  const int64_t bm = mha_impl::fwd_query_block();
+  const int64_t bm = mha_impl::fwd_query_block(dtype == MHA_DTYPE_BF16 ? 1 : 0);
   const int64_t blocks = ((int64_t)N + bm - 1) / bm * (int64_t)B * (int64_t)H;
   if (blocks > INT32_MAX) return MHA_ERR_UNSUPPORTED;
   return MHA_OK;

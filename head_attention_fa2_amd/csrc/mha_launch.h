@@ -6,8 +6,8 @@
 
 namespace mha_impl {
 
-// Query rows per workgroup of the forward kernel.
-int fwd_query_block();
+// Query rows per workgroup of the forward kernel for bf16 (is_bf16 = 1) or fp32 inputs.
+int fwd_query_block(int is_bf16);
 
 // Enqueue the forward kernel; arguments already validated.  Returns the launch status.
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
