@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused MHA fwd TFLOP/s + % of bf16 MFMA peak (B4 H32 N4096 d128 causal)"
 HEADLINE = "bf16_B4_H32_N4096_d128_causal"
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X published dense peaks (bf16 MFMA; fp32 matrix)
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X published dense peaks
 HBM_GBS = 8000.0
 
 
@@ -59,8 +59,9 @@ def _to_device(a, dtype, dev):
     import numpy as np
     import torch
 
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    if dtype in ("bf16", "f16"):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+        return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to(dev)
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
@@ -155,6 +156,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time every workload (lines on stderr)")
+    ap.add_argument("--pages-sweep", action="store_true",
+                    help="also time the fp16 sweep of the paper's FlashAttention-2 figures (lines on stderr)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 5 device-to-device copies of BYTES bytes (to scale HBM counters)")
     args = ap.parse_args()
@@ -225,6 +228,18 @@ def main():
             tf = ww.credited_flops() / (m * 1e-3) / 1e12
             print(json.dumps({"workload": name, "ms": round(m, 5), "TFLOP/s": round(tf, 2),
                               "pct_of_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2),
+                              "parity": parity_sample(ww, rr["inputs"], rr["out"], n=8)}),
+                  file=sys.stderr, flush=True)
+            del rr
+    if args.pages_sweep:
+        for name, ww in mha_inputs.SWEEP.items():
+            steps = max(5, args.steps // 4)
+            rr = time_gpu(ww, steps, 5, dev)
+            m = rr["total_ms"] / steps
+            tf = ww.credited_flops() / (m * 1e-3) / 1e12
+            print(json.dumps({"workload": name, "B": ww.B, "H": ww.H, "N": ww.N, "d": ww.d,
+                              "causal": ww.causal, "ms": round(m, 5), "TFLOP/s": round(tf, 2),
+                              "pct_of_peak": round(100 * tf / PEAK_TFLOPS[ww.dtype], 2),
                               "parity": parity_sample(ww, rr["inputs"], rr["out"], n=8)}),
                   file=sys.stderr, flush=True)
             del rr

@@ -16,13 +16,13 @@ from typing import Optional, Tuple
 
 __all__ = [
     "MHA_OK", "MHA_ERR_INVALID_ARG", "MHA_ERR_UNSUPPORTED", "MHA_ERR_HIP",
-    "MHA_DTYPE_F32", "MHA_DTYPE_BF16",
+    "MHA_DTYPE_F32", "MHA_DTYPE_BF16", "MHA_DTYPE_F16",
     "library_path", "load", "mha_fwd", "mha_fwd_validate", "mha_fwd_flops",
     "mha_fwd_bytes", "mha_status_string", "mha_version", "fwd", "MhaError",
 ]
 
 MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_HIP = 0, 1, 2, 3
-MHA_DTYPE_F32, MHA_DTYPE_BF16 = 0, 1
+MHA_DTYPE_F32, MHA_DTYPE_BF16, MHA_DTYPE_F16 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB: Optional[ctypes.CDLL] = None
@@ -99,21 +99,22 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=None, 
         stream=None) -> Tuple["object", "object"]:
     """``O, LSE = fwd(q, k, v)`` for contiguous ``[B, H, N, d]`` CUDA tensors.
 
-    ``q, k, v``: float32 or bfloat16, same shape, dtype and device.  ``scale`` defaults
+    ``q, k, v``: float32, bfloat16 or float16, same shape, dtype and device.  ``scale`` defaults
     to 1/sqrt(d).  ``out`` / ``lse`` may be given to reuse buffers.  The kernel is
     enqueued on ``stream`` (default: torch's current stream of q's device); the call
     does not synchronise.
     """
     import torch
 
+    _DTYPES = {torch.float32: MHA_DTYPE_F32, torch.bfloat16: MHA_DTYPE_BF16, torch.float16: MHA_DTYPE_F16}
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
     if q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must have the same shape")
     if not (q.is_cuda and k.is_cuda and v.is_cuda) or len({q.device, k.device, v.device}) != 1:
         raise ValueError("q, k, v must be on the same GPU")
-    if q.dtype not in (torch.float32, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must all be float32 or all bfloat16")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float32, all bfloat16 or all float16")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     B, H, N, d = q.shape
@@ -129,7 +130,7 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=None, 
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    dtype = MHA_DTYPE_BF16 if q.dtype == torch.bfloat16 else MHA_DTYPE_F32
+    dtype = _DTYPES[q.dtype]
     with torch.cuda.device(q.device):
         rc = mha_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                      B, H, N, d, int(bool(causal)), float(scale), dtype, stream.cuda_stream)

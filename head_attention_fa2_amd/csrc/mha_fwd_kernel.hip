@@ -56,10 +56,32 @@ namespace mha_impl {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// 16-bit element types: the 8-element operand vector and the 32x32x16 MFMA that
+// consumes it (fp32 accumulate).  fp32 inputs use the fp32 MFMA paths instead.
+template <typename T>
+struct Half16 {
+  typedef bf16x8_t v8;   // unused for fp32
+};
+template <>
+struct Half16<__bf16> {
+  typedef bf16x8_t v8;
+  static __device__ __forceinline__ f32x16_t mma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Half16<_Float16> {
+  typedef f16x8_t v8;
+  static __device__ __forceinline__ f32x16_t mma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 
 constexpr int kQW = 32;                  // query rows per wavefront
 constexpr int kBN = 64;                  // keys per K/V tile
@@ -152,7 +174,8 @@ constexpr int min_waves_per_eu() { return 2 * 2 * kBN * D * (int)sizeof(T) <= 80
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<T, D>())))
 void mha_fwd_kernel(Params p) {
-  constexpr bool kBF16 = sizeof(T) == 2;
+  constexpr bool k16 = sizeof(T) == 2;         // bf16 or fp16 inputs
+  typedef typename Half16<T>::v8 h8_t;
   constexpr int RB = D * (int)sizeof(T);        // bytes per K/V row
   constexpr int R = RB / 16;                     // 16-byte chunks per row
   constexpr int kTileBytes = kBN * RB;
@@ -236,15 +259,15 @@ void mha_fwd_kernel(Params p) {
   // --- Q operand, kept in registers for the whole loop ("Load Q" once).
   // bf16: lane (n, G) holds Q[qrow][16kc + 8G .. +7] for kc = 0..D/16-1.
   // fp32: lane (n, G) holds Q[qrow][8j + 4G .. +3] for j = 0..D/8-1.
-  constexpr int kQF = kBF16 ? D / 16 : D / 8;
-  typedef typename std::conditional<kBF16, bf16x8_t, f32x4_t>::type qfrag_t;
+  constexpr int kQF = k16 ? D / 16 : D / 8;
+  typedef typename std::conditional<k16, h8_t, f32x4_t>::type qfrag_t;
   qfrag_t qf[kQF];
   {
     const bool valid = qrow < N;
     const T* qr = Q + (size_t)(valid ? qrow : 0) * D;
 #pragma unroll
     for (int j = 0; j < kQF; ++j) {
-      const int col = kBF16 ? 16 * j + 8 * G : 8 * j + 4 * G;
+      const int col = k16 ? 16 * j + 8 * G : 8 * j + 4 * G;
       qf[j] = *(const qfrag_t*)(qr + col);
       if (!valid) qf[j] = qfrag_t{};
       // scaled logit = scale * q.k = |scale| * (sign(scale) q).k; multiplying by 1, -1
@@ -264,8 +287,8 @@ void mha_fwd_kernel(Params p) {
   // V^T (A operand of O^T, bf16): ds_read_b64_tr_b16 gathers, in each 16-lane group, a
   // 4-key x 16-column block; source lane s supplies key (s >> 2) and the 4-column group
   // chosen so that output lane m ends up with column sigma(m).
-  int offV[kBF16 ? kDT : 1][2];
-  if constexpr (kBF16) {
+  int offV[k16 ? kDT : 1][2];
+  if constexpr (k16) {
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -287,18 +310,18 @@ void mha_fwd_kernel(Params p) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kBF16) {
+    if constexpr (k16) {
       constexpr int KC = D / 16;
-      bf16x8_t kf[KC][2];
+      h8_t kf[KC][2];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) kf[kc][ks] = *(const bf16x8_t*)(lk + offK[kc] + ks * 32 * RB);
+        for (int ks = 0; ks < 2; ++ks) kf[kc][ks] = *(const h8_t*)(lk + offK[kc] + ks * 32 * RB);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc][ks], qf[kc], s[ks], 0, 0, 0);
+          s[ks] = Half16<T>::mma(kf[kc][ks], qf[kc], s[ks]);
       // schedule: 4 reads, then (2 MFMA, 2 reads) ..., then the last MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -365,15 +388,15 @@ void mha_fwd_kernel(Params p) {
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
     // O^T += V_j^T . P^T
-    if constexpr (kBF16) {
-      bf16x8_t pf[4];   // P^T operand for key chunks kc2 = 2ks + hh (16 keys each)
+    if constexpr (k16) {
+      h8_t pf[4];   // P^T operand for key chunks kc2 = 2ks + hh (16 keys each)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pf[2 * ks + hh][e] = (__bf16)s[ks][8 * hh + e];
-      bf16x8_t vf[4][kDT];
+          for (int e = 0; e < 8; ++e) pf[2 * ks + hh][e] = (T)s[ks][8 * hh + e];
+      h8_t vf[4][kDT];
 #pragma unroll
       for (int kc2 = 0; kc2 < 4; ++kc2)
 #pragma unroll
@@ -382,13 +405,13 @@ void mha_fwd_kernel(Params p) {
               (lds_s16x4_t*)(lv + offV[dt][0] + kc2 * 16 * RB));
           const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_s16x4_t*)(lv + offV[dt][1] + kc2 * 16 * RB));
-          vf[kc2][dt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          vf[kc2][dt] = __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
       for (int kc2 = 0; kc2 < 4; ++kc2)
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc2][dt], pf[kc2], acc[dt], 0, 0, 0);
+          acc[dt] = Half16<T>::mma(vf[kc2][dt], pf[kc2], acc[dt]);
       // schedule: 8 reads (4 operands), then (1 MFMA, 2 reads) ..., then the last MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
@@ -440,16 +463,16 @@ void mha_fwd_kernel(Params p) {
   const float inv = 1.0f / l;
   if (qrow < N) {
     T* orow = (T*)p.o + head + (size_t)qrow * D;
-    if constexpr (kBF16) {
+    if constexpr (k16) {
       // register r of block dt is column 32dt + 16(r>>3) + 8G + (r&7)
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          bf16x8_t ov;
+          h8_t ov;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(acc[dt][8 * hh + e] * inv);
-          *(bf16x8_t*)(orow + dt * 32 + 16 * hh + 8 * G) = ov;
+          for (int e = 0; e < 8; ++e) ov[e] = (T)(acc[dt][8 * hh + e] * inv);
+          *(h8_t*)(orow + dt * 32 + 16 * hh + 8 * G) = ov;
         }
     } else {
       // register r of block dt is column 32dt + 8(r>>2) + 4G + (r&3)
@@ -478,7 +501,7 @@ hipError_t launch(const Params& p, hipStream_t stream) {
 int fwd_query_block(int) { return kBM; }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                      int N, int d, int causal, float scale, int is_bf16, hipStream_t stream) {
+                      int N, int d, int causal, float scale, int dtype, hipStream_t stream) {
   Params p;
   p.q = q;
   p.k = k;
@@ -490,9 +513,13 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
   p.total = p.nqb * B * H;
   p.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
   p.scale2 = (scale != 0.f ? fabsf(scale) : 1.f) * kLog2e;
-  if (is_bf16) {
+  if (dtype == 1) {
     if (d == 64) return causal ? launch<__bf16, 64, true>(p, stream) : launch<__bf16, 64, false>(p, stream);
     return causal ? launch<__bf16, 128, true>(p, stream) : launch<__bf16, 128, false>(p, stream);
+  }
+  if (dtype == 2) {
+    if (d == 64) return causal ? launch<_Float16, 64, true>(p, stream) : launch<_Float16, 64, false>(p, stream);
+    return causal ? launch<_Float16, 128, true>(p, stream) : launch<_Float16, 128, false>(p, stream);
   }
   if (d == 64) return causal ? launch<float, 64, true>(p, stream) : launch<float, 64, false>(p, stream);
   return causal ? launch<float, 128, true>(p, stream) : launch<float, 128, false>(p, stream);

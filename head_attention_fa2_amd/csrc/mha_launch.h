@@ -6,12 +6,13 @@
 
 namespace mha_impl {
 
-// Query rows per workgroup of the forward kernel for bf16 (is_bf16 = 1) or fp32 inputs.
-int fwd_query_block(int is_bf16);
+// Query rows per workgroup of the forward kernel (the same for every element type).
+int fwd_query_block(int dtype);
 
-// Enqueue the forward kernel; arguments already validated.  Returns the launch status.
+// Enqueue the forward kernel; arguments already validated.  dtype: 0 fp32, 1 bf16,
+// 2 fp16 (the mha_dtype values).  Returns the launch status.
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                      int N, int d, int causal, float scale, int is_bf16, hipStream_t stream);
+                      int N, int d, int causal, float scale, int dtype, hipStream_t stream);
 
 }  // namespace mha_impl
 

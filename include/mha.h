@@ -45,9 +45,14 @@ typedef enum mha_status {
 
 typedef enum mha_dtype {
   MHA_DTYPE_F32 = 0,  /* Q, K, V, O float32; all arithmetic in float32 */
-  MHA_DTYPE_BF16 = 1  /* Q, K, V, O bfloat16; products accumulate in float32, the
+  MHA_DTYPE_BF16 = 1, /* Q, K, V, O bfloat16; products accumulate in float32, the
                          softmax runs in float32, P is rounded to bfloat16 (round to
                          nearest even) before the second product, O is rounded once */
+  MHA_DTYPE_F16 = 2   /* Q, K, V, O IEEE float16, as in the paged-attention listing
+                         (ML-Triton paper, section 3.2, Figure 8, which casts P to
+                         float16 before the second product); otherwise as bfloat16:
+                         float32 accumulation and softmax, P and O rounded to float16
+                         (round to nearest even) */
 } mha_dtype;
 
 /*

@@ -7,13 +7,13 @@ Draw recipe (one reading, since the workloads only say "i.i.d. from seed"):
   * ``numpy.random.Generator(PCG64)`` seeded from ``SeedSequence(seed).spawn(3)``,
     one child stream each for Q, K and V, drawn in that order;
   * values are drawn in float32 (normal: ``standard_normal * sigma``; uniform:
-    ``uniform(lo, hi)``), then, for bfloat16 workloads, encoded to bf16 by
+    ``uniform(lo, hi)``), then, for bfloat16 or float16 workloads, encoded by
     round-to-nearest-even on the host;
   * the identical encoded bytes go to the GPU and to the oracle, which decodes
     them exactly.
 
-Arrays are contiguous ``[B, H, N, d]``.  bf16 tensors are returned as ``uint16``
-bit patterns, fp32 tensors as ``float32``.
+Arrays are contiguous ``[B, H, N, d]``.  bf16 and fp16 tensors are returned as
+``uint16`` bit patterns, fp32 tensors as ``float32``.
 """
 from __future__ import annotations
 
@@ -25,7 +25,9 @@ import numpy as np
 __all__ = [
     "Workload",
     "WORKLOADS",
+    "SWEEP",
     "f32_to_bf16_bits",
+    "f32_to_f16_bits",
     "draw",
     "draw_qkv",
 ]
@@ -39,6 +41,13 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Encode float32 values to IEEE float16 bit patterns, round-to-nearest-even
+    (numpy's float32 -> float16 conversion; values beyond 65504 round to inf)."""
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
 @dataclass(frozen=True)
@@ -57,7 +66,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     causal: bool
     seed: int
     qk_dist: Dist = field(default_factory=lambda: Dist("normal", 1.0))
@@ -95,6 +104,20 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+# The FlashAttention-2 forward sweep of the ML-Triton paper (section 4.2, Figures 13
+# and 14): 32k tokens in total, sequence length 1k..32k, hidden size 2048 with head
+# dimension 64 (32 heads) or 128 (16 heads); batch = 32768 / N.  The pages state neither
+# the mask nor the value distribution: both masks are listed, with N(0,1) inputs, in
+# the float16 of the pages' listings.
+SWEEP: Dict[str, Workload] = {}
+for _i, (_d, _causal, _N) in enumerate(
+        (d, c, n) for d in (64, 128) for c in (False, True)
+        for n in (1024, 2048, 4096, 8192, 16384, 32768)):
+    _w = Workload(f"f16_T32k_N{_N}_d{_d}{'_causal' if _causal else ''}", 32768 // _N, 2048 // _d,
+                  _N, _d, "f16", _causal, seed=100 + _i)
+    SWEEP[_w.name] = _w
+
+
 def _sample(rng: np.random.Generator, shape, dist: Dist) -> np.ndarray:
     if dist.kind == "normal":
         x = rng.standard_normal(size=shape, dtype=np.float32)
@@ -110,17 +133,21 @@ def draw(shape, dtype: str, seed: int, qk_dist: Dist = Dist("normal", 1.0),
          v_dist: Dist = Dist("normal", 1.0)) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Draw Q, K, V of ``shape`` (``[B,H,N,d]``) from ``seed``.
 
-    Returns float32 arrays for ``dtype == "f32"`` and uint16 bf16 bit patterns for
-    ``dtype == "bf16"``.
+    Returns float32 arrays for ``dtype == "f32"`` and uint16 bit patterns for
+    ``dtype == "bf16"`` or ``"f16"``.
     """
-    if dtype not in ("f32", "bf16"):
+    if dtype not in ("f32", "bf16", "f16"):
         raise ValueError(f"unknown dtype {dtype!r}")
     children = np.random.SeedSequence(seed).spawn(3)
     out = []
     for child, dist in zip(children, (qk_dist, qk_dist, v_dist)):
         rng = np.random.Generator(np.random.PCG64(child))
         x = _sample(rng, shape, dist)
-        out.append(f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x))
+        if dtype == "bf16":
+            x = f32_to_bf16_bits(x)
+        elif dtype == "f16":
+            x = f32_to_f16_bits(x)
+        out.append(np.ascontiguousarray(x))
     return out[0], out[1], out[2]
 
 

@@ -44,11 +44,24 @@ def decode(x: np.ndarray, dtype: str) -> np.ndarray:
 
     ``dtype == "bf16"``: ``x`` holds bfloat16 bit patterns (uint16); a bf16 value is
     the float32 whose upper 16 bits are the pattern and lower 16 bits are zero.
+    ``dtype == "f16"``: ``x`` holds IEEE binary16 bit patterns (uint16): sign bit,
+    5-bit exponent e (bias 15) and 10-bit fraction f; the value is
+    (-1)^sign * 2^(e-15) * (1 + f/1024) for 0 < e < 31 and (-1)^sign * 2^-14 * f/1024
+    for e = 0 (e = 31, inf/NaN, does not occur in the draws and decodes as inf/NaN).
     ``dtype == "f32"``: ``x`` holds float32 values.  ``dtype == "f64"``: as is.
     """
     if dtype == "bf16":
         bits = np.ascontiguousarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        u = np.ascontiguousarray(x, dtype=np.uint16).astype(np.int64)
+        sign = np.where(u >> 15, -1.0, 1.0)
+        e = (u >> 10) & 0x1F
+        f = (u & 0x3FF).astype(np.float64)
+        normal = sign * np.ldexp(1.0 + f / 1024.0, (e - 15).astype(np.int32))
+        sub = sign * np.ldexp(f / 1024.0, -14)
+        special = np.where(f == 0, sign * np.inf, np.nan)
+        return np.where(e == 0, sub, np.where(e == 31, special, normal))
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "f64":
@@ -116,7 +129,7 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool,
                    ) -> Tuple[np.ndarray, np.ndarray]:
     """O and lse for selected ``(b, h, i)`` query rows only.
 
-    ``q, k, v`` may be encoded (``dtype`` "bf16" / "f32") full-size tensors; only the
+    ``q, k, v`` may be encoded (``dtype`` "bf16" / "f16" / "f32") full-size tensors; only the
     heads that are picked are decoded.  Returns ``(O [P, dv], lse [P])`` float64 in
     the order of ``picks``.  Used to check outputs of workloads too large to
     evaluate whole on the CPU.

@@ -6,12 +6,16 @@ import head_attention_fa2_amd as mha
 import mha_inputs
 import oracle
 
-TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-3)}   # (O, LSE) max abs error
+# (O, LSE) max abs error.  fp16 has unit roundoff 2^-11: rounding P and O costs at
+# most ~2 * 2^-11 * max|V| ~ 4e-3 for the N(0,1) values drawn here, so 5e-3.
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-3), "f16": (5e-3, 1e-3)}
 
 
 def to_device(a: np.ndarray, dtype: str, dev="cuda:0"):
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    if dtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).to(dev)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
 

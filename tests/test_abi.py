@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mha.h")
 
 OK, INVALID, UNSUPPORTED = mha.MHA_OK, mha.MHA_ERR_INVALID_ARG, mha.MHA_ERR_UNSUPPORTED
-BF16, F32 = mha.MHA_DTYPE_BF16, mha.MHA_DTYPE_F32
+BF16, F32, F16 = mha.MHA_DTYPE_BF16, mha.MHA_DTYPE_F32, mha.MHA_DTYPE_F16
 P = 0x10000  # a 16-byte aligned fake address (never dereferenced by validation)
 
 
@@ -49,13 +49,14 @@ def v(**kw):
 def test_validate_accepts_good_arguments():
     assert v() == OK
     assert v(d=128, causal=1, dtype=F32) == OK
+    assert v(d=128, causal=1, dtype=F16) == OK
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), INVALID), (dict(k=0), INVALID), (dict(v=0), INVALID), (dict(o=0), INVALID),
     (dict(lse=0), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID),
     (dict(causal=2), INVALID), (dict(scale=float("nan")), INVALID),
-    (dict(scale=float("inf")), INVALID), (dict(dtype=7), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(dtype=7), INVALID), (dict(dtype=3), INVALID),
     (dict(d=32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
     (dict(q=P + 8), UNSUPPORTED), (dict(o=P + 4), UNSUPPORTED), (dict(lse=P + 2), UNSUPPORTED),
     (dict(B=65536, H=65536, N=1 << 20), UNSUPPORTED),
@@ -75,6 +76,7 @@ def test_flops_and_bytes():
     assert mha.mha_fwd_flops(4, 16, 1024, 64, 0) == 4 * 4 * 16 * 1024 ** 2 * 64
     assert mha.mha_fwd_bytes(4, 32, 4096, 128, BF16) == 4 * 4 * 32 * 4096 * 128 * 2 + 4 * 4 * 32 * 4096
     assert mha.mha_fwd_bytes(1, 2, 128, 64, F32) == 4 * 2 * 128 * 64 * 4 + 4 * 2 * 128
+    assert mha.mha_fwd_bytes(2, 16, 1024, 128, F16) == 4 * 2 * 16 * 1024 * 128 * 2 + 4 * 2 * 16 * 1024
 
 
 def test_status_strings():

@@ -1,6 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on identical
 seeded inputs.  Tolerances: fp32 inputs max|dO|, max|dLSE| <= 1e-4; bf16 inputs
-max|dO| <= 2e-2, max|dLSE| <= 1e-3."""
+max|dO| <= 2e-2, max|dLSE| <= 1e-3; fp16 inputs max|dO| <= 5e-3, max|dLSE| <= 1e-3."""
 import math
 
 import numpy as np
@@ -38,6 +38,19 @@ SMALL = [
     ("bf16_B1_H32_N16384_d128_causal", dict(B=1, H=2, N=2049)),
     ("bf16_B8_H16_N8192_d64_stress", dict(B=2, H=2, N=1100)),
 ]
+
+
+# fp16 inputs (the element type of the pages' listings), several tiles and ragged tails
+SMALL_F16 = [(1, 2, 1000, 128, True), (2, 3, 777, 64, False), (1, 4, 1100, 128, False), (2, 2, 300, 64, True)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SMALL_F16)
+def test_f16_elementwise(B, H, N, d, causal):
+    q, k, v = gu.draw(B, H, N, d, "f16", seed=500 + N + d)
+    scale = 1 / math.sqrt(d)
+    o, lse = gu.run(q, k, v, "f16", causal, scale)
+    o_ref, l_ref = gu.oracle_full(q, k, v, "f16", causal, scale)
+    _check(o, lse, o_ref, l_ref, "f16", f"f16 B{B} H{H} N{N} d{d} causal={causal}")
 
 
 @pytest.mark.parametrize("name,shape", SMALL, ids=[s[0] for s in SMALL])
@@ -84,7 +97,7 @@ def test_workload_full_size_sampled(name):
 
 # ---------------------------------------------------------------- edge cases
 EDGE = []
-for dtype in ("bf16", "f32"):
+for dtype in ("bf16", "f32", "f16"):
     for d in (64, 128):
         for N in (1, 2, 63, 64, 65, 127, 129, 200, 257):
             for causal in (False, True):
@@ -101,7 +114,7 @@ def test_edge_shapes(B, H, N, d, causal, dtype):
     _check(o, lse, o_ref, l_ref, dtype, f"edge B{B} H{H} N{N} d{d} causal={causal} {dtype}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_scales_and_large_logits(dtype):
     B, H, N, d = 1, 2, 300, 64
     for sigma, scale in ((3.0, 0.125), (1.0, 1.0), (1.0, -0.3), (5.0, 0.5)):
@@ -116,14 +129,15 @@ def test_scales_and_large_logits(dtype):
 
 
 # ---------------------------------------------------------------- invariants on GPU output
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_invariants_on_gpu(dtype, d):
     B, H, N = 1, 2, 333
     tol_o, tol_l = gu.TOL[dtype]
     q, k, v = gu.draw(B, H, N, d, dtype, seed=5)
-    ones = mha_inputs.f32_to_bf16_bits(np.ones_like(v, dtype=np.float32)) if dtype == "bf16" \
-        else np.ones(v.shape, dtype=np.float32)
+    enc = {"bf16": mha_inputs.f32_to_bf16_bits, "f16": mha_inputs.f32_to_f16_bits,
+           "f32": lambda x: x}[dtype]
+    ones = enc(np.ones(v.shape, dtype=np.float32))
     zeros = np.zeros_like(q)
     vf = oracle.decode(v, dtype)
     for causal in (False, True):
@@ -175,6 +189,6 @@ def test_errors_raise():
         mha.fwd(q, q, q)
     assert e.value.status == mha.MHA_ERR_UNSUPPORTED
     with pytest.raises(ValueError):
-        mha.fwd(q.half(), q.half(), q.half())
+        mha.fwd(q.double(), q.double(), q.double())
     with pytest.raises(ValueError):
         mha.fwd(q, q.float(), q)

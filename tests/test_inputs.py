@@ -17,6 +17,19 @@ def test_bf16_encoder_matches_torch_rne():
     assert ours[-5] == 0x3F80 and ours[-4] == 0x3F82
 
 
+def test_f16_encoder_matches_torch_rne():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([0.0, -0.0, 1.0, 1.00048828125, 1.00146484375, 65504.0, 6.0e-8, 7.0e4],
+                                 dtype=np.float32)])
+    # exact ties: 1 + 2^-11 rounds to 1 (even), 1 + 3*2^-11 rounds up to 1 + 2^-9;
+    # 7e4 overflows to inf
+    ours = mi.f32_to_f16_bits(x)
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert ours[-6] == 0x3C00 and ours[-5] == 0x3C00 and ours[-4] == 0x3C02 and ours[-1] == 0x7C00
+
+
 def test_draw_is_deterministic_and_seed_dependent():
     a = mi.draw((1, 2, 8, 4), "bf16", 3)
     b = mi.draw((1, 2, 8, 4), "bf16", 3)
@@ -43,3 +56,14 @@ def test_named_workloads():
     assert (w.B, w.H, w.N, w.d, w.causal, w.dtype) == (4, 32, 4096, 128, True, "bf16")
     assert w.credited_flops() == 4 * 4 * 32 * 4096 * 4096 * 128 / 2
     assert abs(w.scale - 1 / np.sqrt(128)) < 1e-15
+
+
+def test_pages_sweep_table():
+    # 32k tokens, sequence 1k..32k, hidden 2048 = H * d with d in {64, 128}, both masks
+    assert len(mi.SWEEP) == 24
+    for w in mi.SWEEP.values():
+        assert w.B * w.N == 32768 and w.H * w.d == 2048 and w.dtype == "f16"
+        assert w.N in (1024, 2048, 4096, 8192, 16384, 32768) and w.d in (64, 128)
+    assert len({w.seed for w in mi.SWEEP.values()}) == 24
+    q = mi.draw((1, 1, 8, 8), "f16", 3)[0]
+    assert q.dtype == np.uint16

@@ -55,6 +55,34 @@ def test_decode_bf16_exact():
     assert np.array_equal(got, want) and np.signbit(got[5])
 
 
+def test_decode_f16_exact():
+    # binary16 patterns: sign | 5-bit exponent (bias 15) | 10-bit fraction; 0x3C00 = 1.0,
+    # 0xC000 = -2.0, 0x0001 = smallest subnormal 2^-24, 0x03FF = largest subnormal
+    # 1023 * 2^-24, 0x0400 = smallest normal 2^-14, 0x7BFF = largest finite 65504,
+    # 0x3555 = 1365/4096 (the float16 nearest 1/3)
+    bits = np.array([0x3C00, 0xC000, 0x0001, 0x03FF, 0x0400, 0x7BFF, 0x3555, 0x8000], dtype=np.uint16)
+    want = np.array([1.0, -2.0, 2.0 ** -24, 1023 * 2.0 ** -24, 2.0 ** -14, 65504.0, 1365 / 4096, -0.0])
+    got = oracle.decode(bits, "f16")
+    assert np.array_equal(got, want) and np.signbit(got[7])
+    # every finite pattern agrees with the IEEE conversion of a library (numpy's float16)
+    allbits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((allbits >> 10) & 0x1F) != 31
+    assert np.array_equal(oracle.decode(allbits[finite], "f16"),
+                          allbits[finite].view(np.float16).astype(np.float64))
+
+
+def test_bruteforce_decimal_on_f16_inputs():
+    # float16-encoded inputs go through the same definition: decode exactly, then compare
+    # with the 40-digit decimal evaluation of the definition
+    rng = np.random.default_rng(11)
+    bits = [rng.standard_normal((1, 2, 9, 5)).astype(np.float16).view(np.uint16) for _ in range(3)]
+    q, k, v = (oracle.decode(b, "f16") for b in bits)
+    for causal in (False, True):
+        o, lse = oracle.attention_forward(q, k, v, causal=causal, scale=0.7)
+        o_ref, lse_ref = pins.decimal_attention(q, k, v, causal, 0.7)
+        assert np.max(np.abs(o - o_ref)) <= 1e-12 and np.max(np.abs(lse - lse_ref)) <= 1e-12
+
+
 def test_causal_requires_square():
     q, k, v = pins.rand_qkv(1, 1, 1, 4, 4, Nk=5)
     with pytest.raises(ValueError):
