@@ -93,6 +93,32 @@ def time_gpu(w, steps, warmup, dev):
     return dict(total_ms=total_ms, per_ms=per, wall_s=wall, inputs=(q, k, v), out=(o, lse))
 
 
+def time_gpu_splitkv(w, steps, warmup, dev):
+    """As time_gpu, for the split-KV forward of a decode workload (library's split count)."""
+    import torch
+
+    import head_attention_fa2_amd as mha
+    import mha_inputs
+
+    q, k, v = mha_inputs.draw_qkv(w)
+    tq, tk, tv = (_to_device(x, w.dtype, dev) for x in (q, k, v))
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(mha.mha_fwd_splitkv_workspace_size(w.B, w.H, w.N, w.Nk, w.d, 0), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        mha.fwd_splitkv(tq, tk, tv, scale=w.scale, out=o, lse=lse, workspace=ws, stream=stream)
+    torch.cuda.synchronize(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        mha.fwd_splitkv(tq, tk, tv, scale=w.scale, out=o, lse=lse, workspace=ws, stream=stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    return dict(total_ms=ev[0].elapsed_time(ev[steps]), inputs=(q, k, v), out=(o, lse))
+
+
 def parity_sample(w, inputs, out, n=24):
     """Max abs error of sampled output rows against the CPU oracle."""
     import numpy as np
@@ -105,6 +131,7 @@ def parity_sample(w, inputs, out, n=24):
     rng = np.random.default_rng(123)
     picks = [(int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.N))) for _ in range(n)]
     picks += [(0, 0, 0), (w.B - 1, w.H - 1, w.N - 1)]
+    picks = sorted(set(picks))
     o_ref, l_ref = oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, picks=picks, dtype=w.dtype)
     idx = torch.tensor(picks, dtype=torch.long, device=o.device)
     og = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy()
@@ -156,6 +183,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time every workload (lines on stderr)")
+    ap.add_argument("--decode", action="store_true",
+                    help="also time the split-KV decode workloads (lines on stderr)")
     ap.add_argument("--pages-sweep", action="store_true",
                     help="also time the fp16 sweep of the paper's FlashAttention-2 figures (lines on stderr)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -228,6 +257,21 @@ def main():
             tf = ww.credited_flops() / (m * 1e-3) / 1e12
             print(json.dumps({"workload": name, "ms": round(m, 5), "TFLOP/s": round(tf, 2),
                               "pct_of_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2),
+                              "parity": parity_sample(ww, rr["inputs"], rr["out"], n=8)}),
+                  file=sys.stderr, flush=True)
+            del rr
+    if args.decode:
+        for name, ww in mha_inputs.DECODE.items():
+            steps = max(10, args.steps // 2)
+            rr = time_gpu_splitkv(ww, steps, 10, dev)
+            m = rr["total_ms"] / steps
+            nbytes = mha.mha_fwd_splitkv_bytes(ww.B, ww.H, ww.N, ww.Nk, ww.d,
+                                               {"f32": 0, "bf16": 1, "f16": 2}[ww.dtype])
+            print(json.dumps({"workload": name, "B": ww.B, "H": ww.H, "Nq": ww.N, "Nk": ww.Nk, "d": ww.d,
+                              "splits": mha.mha_fwd_splitkv_splits(ww.B, ww.H, ww.N, ww.Nk, 0),
+                              "ms": round(m, 5), "GB/s": round(nbytes / (m * 1e-3) / 1e9, 1),
+                              "pct_of_hbm": round(100 * nbytes / (m * 1e-3) / 1e9 / HBM_GBS, 2),
+                              "TFLOP/s": round(ww.credited_flops() / (m * 1e-3) / 1e12, 2),
                               "parity": parity_sample(ww, rr["inputs"], rr["out"], n=8)}),
                   file=sys.stderr, flush=True)
             del rr

@@ -3,9 +3,11 @@
 The compute is entirely in ``libmha.so`` (hand-written HIP kernels for gfx950 behind
 the C ABI of ``include/mha.h``).  This module only marshals arguments: the functions
 ``mha_fwd``, ``mha_fwd_validate``, ``mha_fwd_flops``, ``mha_fwd_bytes``,
-``mha_status_string`` and ``mha_version`` mirror the C entry points one to one, and
-:func:`fwd` is the PyTorch-facing convenience (device memory and the stream come from
-torch; nothing is computed in Python).  There is no fallback: if the library is not
+``mha_fwd_splitkv``, ``mha_fwd_splitkv_validate``, ``mha_fwd_splitkv_splits``,
+``mha_fwd_splitkv_workspace_size``, ``mha_fwd_splitkv_bytes``, ``mha_status_string``
+and ``mha_version`` mirror the C entry points one to one, and :func:`fwd` /
+:func:`fwd_splitkv` are the PyTorch-facing conveniences (device memory and the stream
+come from torch; nothing is computed in Python).  There is no fallback: if the library is not
 built or a call fails, an exception is raised.
 """
 from __future__ import annotations
@@ -18,7 +20,9 @@ __all__ = [
     "MHA_OK", "MHA_ERR_INVALID_ARG", "MHA_ERR_UNSUPPORTED", "MHA_ERR_HIP",
     "MHA_DTYPE_F32", "MHA_DTYPE_BF16", "MHA_DTYPE_F16",
     "library_path", "load", "mha_fwd", "mha_fwd_validate", "mha_fwd_flops",
-    "mha_fwd_bytes", "mha_status_string", "mha_version", "fwd", "MhaError",
+    "mha_fwd_bytes", "mha_fwd_splitkv", "mha_fwd_splitkv_validate", "mha_fwd_splitkv_splits",
+    "mha_fwd_splitkv_workspace_size", "mha_fwd_splitkv_bytes", "mha_status_string", "mha_version",
+    "fwd", "fwd_splitkv", "MhaError",
 ]
 
 MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_HIP = 0, 1, 2, 3
@@ -58,6 +62,17 @@ def load() -> ctypes.CDLL:
     lib.mha_fwd_flops.restype = ctypes.c_double
     lib.mha_fwd_bytes.argtypes = [i, i, i, i, i]
     lib.mha_fwd_bytes.restype = ctypes.c_double
+    sz = ctypes.c_size_t
+    lib.mha_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.mha_fwd_splitkv.restype = i
+    lib.mha_fwd_splitkv_validate.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz]
+    lib.mha_fwd_splitkv_validate.restype = i
+    lib.mha_fwd_splitkv_splits.argtypes = [i, i, i, i, i]
+    lib.mha_fwd_splitkv_splits.restype = i
+    lib.mha_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.mha_fwd_splitkv_workspace_size.restype = sz
+    lib.mha_fwd_splitkv_bytes.argtypes = [i, i, i, i, i, i]
+    lib.mha_fwd_splitkv_bytes.restype = ctypes.c_double
     lib.mha_status_string.argtypes = [i]
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_version.argtypes = []
@@ -84,6 +99,33 @@ def mha_fwd_flops(B: int, H: int, N: int, d: int, causal: int) -> float:
 
 def mha_fwd_bytes(B: int, H: int, N: int, d: int, dtype: int) -> float:
     return load().mha_fwd_bytes(B, H, N, d, dtype)
+
+
+def mha_fwd_splitkv(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int,
+                    d: int, scale: float, dtype: int, splits: int, workspace: int,
+                    workspace_bytes: int, stream: int) -> int:
+    """Enqueue the split-KV forward (partials, then the merge) on ``stream``."""
+    return load().mha_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits,
+                                  workspace, workspace_bytes, stream)
+
+
+def mha_fwd_splitkv_validate(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int,
+                             Nk: int, d: int, scale: float, dtype: int, splits: int,
+                             workspace: int, workspace_bytes: int) -> int:
+    return load().mha_fwd_splitkv_validate(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits,
+                                           workspace, workspace_bytes)
+
+
+def mha_fwd_splitkv_splits(B: int, H: int, Nq: int, Nk: int, splits: int) -> int:
+    return load().mha_fwd_splitkv_splits(B, H, Nq, Nk, splits)
+
+
+def mha_fwd_splitkv_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, splits: int) -> int:
+    return load().mha_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, splits)
+
+
+def mha_fwd_splitkv_bytes(B: int, H: int, Nq: int, Nk: int, d: int, dtype: int) -> float:
+    return load().mha_fwd_splitkv_bytes(B, H, Nq, Nk, d, dtype)
 
 
 def mha_status_string(status: int) -> str:
@@ -136,4 +178,53 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=None, 
                      B, H, N, d, int(bool(causal)), float(scale), dtype, stream.cuda_stream)
     if rc != MHA_OK:
         raise MhaError(rc)
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, scale: Optional[float] = None, splits: int = 0, out=None, lse=None,
+                workspace=None, stream=None) -> Tuple["object", "object"]:
+    """``O, LSE = fwd_splitkv(q, k, v)``: ``q`` ``[B, H, Nq, d]`` against ``k, v``
+    ``[B, H, Nk, d]`` (contiguous CUDA tensors of one dtype), no mask, with the keys cut
+    into ``splits`` ranges (0: the library's choice).  ``workspace`` (a CUDA tensor of at
+    least :func:`mha_fwd_splitkv_workspace_size` bytes) is allocated through torch when
+    not given.  Enqueued on ``stream`` (default: torch's current stream); no sync.
+    """
+    import torch
+
+    _DTYPES = {torch.float32: MHA_DTYPE_F32, torch.bfloat16: MHA_DTYPE_BF16, torch.float16: MHA_DTYPE_F16}
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] with the batch, heads and d of q")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or len({q.device, k.device, v.device}) != 1:
+        raise ValueError("q, k, v must be on the same GPU")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float32, all bfloat16 or all float16")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    need = mha_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = mha_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, H, Nq, Nk, d, float(scale), _DTYPES[q.dtype], int(splits),
+                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                         stream.cuda_stream)
+    if st != MHA_OK:
+        raise MhaError(st)
     return out, lse

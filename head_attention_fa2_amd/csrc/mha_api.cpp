@@ -3,6 +3,7 @@
 #include "mha.h"
 
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 
 #include "mha_launch.h"
@@ -27,6 +28,53 @@ mha_status validate(const void* q, const void* k, const void* v, const void* o, 
   return MHA_OK;
 }
 
+// Split-KV partition: `splits` requested (0 = automatic), resolved to key ranges of
+// `chunk` keys (a multiple of the 64-key tile) and the number of non-empty ranges.
+// Automatic: enough ranges for about 512 workgroups (two per CU of the MI355X), each of
+// at least 512 keys.
+struct Partition {
+  int splits;
+  int chunk;
+};
+Partition partition(int B, int H, int Nq, int Nk, int splits) {
+  const int64_t bm = mha_impl::fwd_query_block(1);
+  const int64_t blocks = ((int64_t)Nq + bm - 1) / bm * (int64_t)B * (int64_t)H;
+  int64_t s = splits;
+  if (s <= 0) {
+    s = (512 + blocks - 1) / blocks;
+    const int64_t cap = ((int64_t)Nk + 511) / 512;
+    if (s > cap) s = cap;
+  }
+  const int64_t tiles = ((int64_t)Nk + 63) / 64;
+  if (s > tiles) s = tiles;
+  if (s < 1) s = 1;
+  const int64_t chunk = (tiles + s - 1) / s * 64;
+  return Partition{(int)(((int64_t)Nk + chunk - 1) / chunk), (int)chunk};
+}
+
+size_t workspace_bytes(int B, int H, int Nq, int d, int splits) {
+  return (size_t)splits * (size_t)B * (size_t)H * (size_t)Nq * ((size_t)d + 1) * sizeof(float);
+}
+
+mha_status validate_splitkv(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                            int B, int H, int Nq, int Nk, int d, float scale, mha_dtype dtype, int splits,
+                            const void* workspace, size_t ws_bytes) {
+  if (!q || !k || !v || !o || !lse || !workspace) return MHA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || splits < 0) return MHA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MHA_ERR_INVALID_ARG;
+  if (dtype != MHA_DTYPE_F32 && dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_F16) return MHA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return MHA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return MHA_ERR_UNSUPPORTED;
+  const Partition pt = partition(B, H, Nq, Nk, splits);
+  if (ws_bytes < workspace_bytes(B, H, Nq, d, pt.splits)) return MHA_ERR_INVALID_ARG;
+  const int64_t bm = mha_impl::fwd_query_block((int)dtype);
+  const int64_t blocks = ((int64_t)Nq + bm - 1) / bm * (int64_t)B * (int64_t)H * pt.splits;
+  if (blocks > INT32_MAX || (int64_t)B * H * Nq > INT32_MAX) return MHA_ERR_UNSUPPORTED;
+  return MHA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -44,6 +92,42 @@ mha_status mha_fwd(const void* q, const void* k, const void* v, void* o, float* 
   const hipError_t e = mha_impl::launch_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, (int)dtype,
                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+int mha_fwd_splitkv_splits(int B, int H, int Nq, int Nk, int splits) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || splits < 0) return 0;
+  return partition(B, H, Nq, Nk, splits).splits;
+}
+
+size_t mha_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int splits) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || splits < 0 || d < 1) return 0;
+  return workspace_bytes(B, H, Nq, d, partition(B, H, Nq, Nk, splits).splits);
+}
+
+mha_status mha_fwd_splitkv_validate(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                                    mha_dtype dtype, int splits, const void* workspace,
+                                    size_t workspace_bytes) {
+  return validate_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits, workspace, workspace_bytes);
+}
+
+mha_status mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                           int Nq, int Nk, int d, float scale, mha_dtype dtype, int splits, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const mha_status st =
+      validate_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits, workspace, workspace_bytes);
+  if (st != MHA_OK) return st;
+  const Partition pt = partition(B, H, Nq, Nk, splits);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = part_o + (size_t)pt.splits * B * H * Nq * d;
+  const hipError_t e = mha_impl::launch_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, (int)dtype, pt.splits,
+                                                    pt.chunk, part_o, part_lse, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+double mha_fwd_splitkv_bytes(int B, int H, int Nq, int Nk, int d, mha_dtype dtype) {
+  const double elem = dtype == MHA_DTYPE_F32 ? 4.0 : 2.0;
+  return (2.0 * Nq + 2.0 * Nk) * B * H * (double)d * elem + 4.0 * B * H * (double)Nq;
 }
 
 double mha_fwd_flops(int B, int H, int N, int d, int causal) {

@@ -98,11 +98,19 @@ struct Params {
   const void* v;
   void* o;
   float* lse;
-  int N;          // sequence length
+  int N;          // query rows per head (= keys per head, except for the split-KV kernel)
   int nqb;        // query blocks per head
   int total;      // workgroups
   float qmul;     // sign(scale): Q is multiplied by it on load (1, -1 or 0)
   float scale2;   // |scale| * log2(e), or log2(e) when scale == 0
+  // split-KV only: keys per head, keys per split (a multiple of the tile), number of
+  // splits, B*H, and the float32 partial results [split][B*H][N][d] and [split][B*H][N]
+  int Nk;
+  int chunk;
+  int splits;
+  int BH;
+  float* part_o;
+  float* part_lse;
 };
 
 // ---------------------------------------------------------------------------- LDS layout
@@ -171,9 +179,13 @@ __device__ __forceinline__ void tile_barrier() {
 template <typename T, int D>
 constexpr int min_waves_per_eu() { return 2 * 2 * kBN * D * (int)sizeof(T) <= 80 * 1024 ? 2 : 1; }
 
-template <typename T, int D, bool CAUSAL>
+// SPLIT: the split-KV form (no mask): workgroup (split, head, query block) covers the
+// keys [split * chunk, min(Nk, (split + 1) * chunk)) and writes its O (normalised by its
+// own l) and logsumexp to the float32 partial buffers; mha_merge_kernel combines them.
+template <typename T, int D, bool CAUSAL, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<T, D>())))
 void mha_fwd_kernel(Params p) {
+  static_assert(!(SPLIT && CAUSAL), "the split-KV form has no mask");
   constexpr bool k16 = sizeof(T) == 2;         // bf16 or fp16 inputs
   typedef typename Half16<T>::v8 h8_t;
   constexpr int RB = D * (int)sizeof(T);        // bytes per K/V row
@@ -195,20 +207,29 @@ void mha_fwd_kernel(Params p) {
   // keeps every head's query blocks on one XCD.  Causal: latest (heaviest) blocks first.
   int id = blockIdx.x;
   if ((p.total & 7) == 0) id = (id & 7) * (p.total >> 3) + (id >> 3);
+  int split = 0;
+  if constexpr (SPLIT) {
+    split = id / (p.nqb * p.BH);
+    id -= split * p.nqb * p.BH;
+  }
   const int bh = id / p.nqb;
   int qb = id - bh * p.nqb;
   if (CAUSAL) qb = p.nqb - 1 - qb;
-  const int N = p.N;
+  const int N = p.N;                            // query rows
+  const int Nk = SPLIT ? p.Nk : N;              // keys
+  const int kbeg = SPLIT ? split * p.chunk : 0; // this workgroup's keys: [kbeg, kend)
+  const int kend = SPLIT ? min(Nk, kbeg + p.chunk) : N;
   const int q0 = qb * kBM;
   const int qw = q0 + wave * kQW;               // first query row of this wavefront
   const int qrow = qw + n;                      // the query row this lane owns
   const size_t head = (size_t)bh * (size_t)N * D;
+  const size_t khead = SPLIT ? (size_t)bh * (size_t)Nk * D : head;
   const T* __restrict__ Q = (const T*)p.q + head;
-  const char* Kbase = (const char*)((const T*)p.k + head);
-  const char* Vbase = (const char*)((const T*)p.v + head);
+  const char* Kbase = (const char*)((const T*)p.k + khead);
+  const char* Vbase = (const char*)((const T*)p.v + khead);
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
-  const int ntiles = (kv_end + kBN - 1) / kBN;
+  const int kv_end = CAUSAL ? min(N, q0 + kBM) : kend;
+  const int ntiles = (kv_end - kbeg + kBN - 1) / kBN;
 
   // --- tile loader: thread (wave, lane) copies kLoads 16-byte chunks of K and of V.
   // Load j of a thread fills LDS bytes [(j*kWaves + wave)*1024, +1024); the swizzle is
@@ -228,12 +249,12 @@ void mha_fwd_kernel(Params p) {
   const int ld_row0 = ld_row[0];
   const unsigned ld_off0 = (unsigned)(ld_row0 * RB + ld_chunk[0] * 16);
   auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
-    const int k0 = t * kBN;
+    const int k0 = kbeg + t * kBN;
     const char* kg = Kbase + (size_t)k0 * RB;
     const char* vg = Vbase + (size_t)k0 * RB;
     char* lk = smem + buf * 2 * kTileBytes;
     char* lv = lk + kTileBytes;
-    if (k0 + kBN <= N) {
+    if (k0 + kBN <= kend) {
 #pragma unroll
       for (int j = 0; j < kLoads; ++j) {
         const unsigned off = mha_layout::loader_periodic<R>()
@@ -244,10 +265,10 @@ void mha_fwd_kernel(Params p) {
         copy_to_lds(vg, off, lds_addr(lv + dst));
       }
     } else {
-      // ragged last tile: rows past the end re-read row N-1 (finite, masked later)
+      // ragged last tile: rows past the end re-read the last key (finite, masked later)
 #pragma unroll
       for (int j = 0; j < kLoads; ++j) {
-        const int row = min(k0 + ld_row[j], N - 1) - k0;
+        const int row = min(k0 + ld_row[j], kend - 1) - k0;
         const unsigned off = (unsigned)(row * RB + ld_chunk[j] * 16);
         const int dst = (j * kWaves + wave) * 1024;
         copy_to_lds(kg, off, lds_addr(lk + dst));
@@ -347,7 +368,7 @@ void mha_fwd_kernel(Params p) {
     // Mask: accumulator register r of slab ks on lane half G is key
     // k0 + 32ks + 16(r>>3) + 8G + (r&7).
     if (masked) {
-      const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+      const int lim = CAUSAL ? min(qrow, N - 1) : kend - 1;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -446,9 +467,10 @@ void mha_fwd_kernel(Params p) {
     wait_vmcnt<0>();
     tile_barrier();
     if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
-    const int k0 = t * kBN;
+    const int k0 = kbeg + t * kBN;
+    if (SPLIT && qw >= N) return;                      // no query row in this wavefront
     if (!CAUSAL || k0 <= qw + kQW - 1) {               // else: every key is after every row
-      const bool need_mask = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > qw);
+      const bool need_mask = (k0 + kBN > kend) || (CAUSAL && k0 + kBN - 1 > qw);
       compute_tile(smem + buf * 2 * kTileBytes, smem + buf * 2 * kTileBytes + kTileBytes, k0, need_mask);
     }
   };
@@ -461,6 +483,27 @@ void mha_fwd_kernel(Params p) {
   // --- epilogue: O = acc / l, lse = m + ln l, each written once.
   const float l = sum_halves(l_run);
   const float inv = 1.0f / l;
+  if constexpr (SPLIT) {
+    // partial result of this key range: O_s = acc / l (float32) and lse_s = m + ln l
+    if (qrow < N) {
+      const size_t r = ((size_t)split * p.BH + bh) * (size_t)N + qrow;
+      float* orow = p.part_o + r * D;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4_t ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = acc[dt][4 * g + e] * inv;
+          // register r of block dt: 16-bit inputs column 32dt + 16(r>>3) + 8G + (r&7),
+          // fp32 inputs column 32dt + 8(r>>2) + 4G + (r&3)
+          const int col = k16 ? dt * 32 + 16 * (g >> 1) + 8 * G + 4 * (g & 1) : dt * 32 + 8 * g + 4 * G;
+          *(f32x4_t*)(orow + col) = ov;
+        }
+      if (G == 0) p.part_lse[r] = (m_run * c2 + __builtin_amdgcn_logf(l)) * kLn2;
+    }
+    return;
+  }
   if (qrow < N) {
     T* orow = (T*)p.o + head + (size_t)qrow * D;
     if constexpr (k16) {
@@ -496,6 +539,37 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Merge of the split-KV partial results (the cross-partition reduction of split-KV
+// decoding): for one query row with partials (O_s, lse_s), s = 0..S-1,
+//   lse = M + ln(sum_s exp(lse_s - M)),  M = max_s lse_s,
+//   O   = sum_s exp(lse_s - lse) * O_s.
+// One workgroup of D threads per row; thread c produces column c.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void mha_merge_kernel(Params p) {
+  const size_t row = blockIdx.x;                      // (b*H + h) * N + query row
+  const size_t stride = (size_t)p.BH * (size_t)p.N;   // between splits
+  const int c = threadIdx.x;
+  float m = -__builtin_inff();
+  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_lse[s * stride + row]);
+  float wsum = 0.f, o = 0.f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float w = __builtin_amdgcn_exp2f((p.part_lse[s * stride + row] - m) * kLog2e);
+    wsum += w;
+    o += w * p.part_o[(s * stride + row) * D + c];
+  }
+  ((T*)p.o)[row * D + c] = (T)(o / wsum);
+  if (c == 0) p.lse[row] = m + __builtin_amdgcn_logf(wsum) * kLn2;
+}
+
+template <typename T, int D>
+hipError_t launch_split(const Params& p, hipStream_t stream) {
+  hipLaunchKernelGGL((mha_fwd_kernel<T, D, false, true>), dim3(p.total), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mha_merge_kernel<T, D>), dim3(p.BH * p.N), dim3(D), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int fwd_query_block(int) { return kBM; }
@@ -523,6 +597,31 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
   }
   if (d == 64) return causal ? launch<float, 64, true>(p, stream) : launch<float, 64, false>(p, stream);
   return causal ? launch<float, 128, true>(p, stream) : launch<float, 128, false>(p, stream);
+}
+
+hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                              int Nq, int Nk, int d, float scale, int dtype, int splits, int chunk,
+                              float* part_o, float* part_lse, hipStream_t stream) {
+  Params p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.N = Nq;
+  p.nqb = (Nq + kBM - 1) / kBM;
+  p.Nk = Nk;
+  p.chunk = chunk;
+  p.splits = splits;
+  p.BH = B * H;
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  p.total = p.nqb * p.BH * splits;
+  p.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
+  p.scale2 = (scale != 0.f ? fabsf(scale) : 1.f) * kLog2e;
+  if (dtype == 1) return d == 64 ? launch_split<__bf16, 64>(p, stream) : launch_split<__bf16, 128>(p, stream);
+  if (dtype == 2) return d == 64 ? launch_split<_Float16, 64>(p, stream) : launch_split<_Float16, 128>(p, stream);
+  return d == 64 ? launch_split<float, 64>(p, stream) : launch_split<float, 128>(p, stream);
 }
 
 }  // namespace mha_impl

@@ -14,6 +14,13 @@ int fwd_query_block(int dtype);
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                       int N, int d, int causal, float scale, int dtype, hipStream_t stream);
 
+// Enqueue the split-KV forward (no mask; Nq query rows against Nk keys per head): the
+// partial kernel over `splits` key ranges of `chunk` keys, then the merge.  part_o /
+// part_lse: float32 [splits][B*H][Nq][d] and [splits][B*H][Nq].  Arguments validated.
+hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                              int Nq, int Nk, int d, float scale, int dtype, int splits, int chunk,
+                              float* part_o, float* part_lse, hipStream_t stream);
+
 }  // namespace mha_impl
 
 #endif  // MHA_LAUNCH_H_

@@ -30,6 +30,8 @@
 #ifndef MHA_H_
 #define MHA_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -96,6 +98,63 @@ double mha_fwd_flops(int B, int H, int N, int d, int causal);
  * written once (B*H*N*d elements each) plus the float32 LSE.  Pure host function.
  */
 double mha_fwd_bytes(int B, int H, int N, int d, mha_dtype dtype);
+
+/*
+ * Split-KV forward (decoding with a long key/value sequence).
+ *
+ * The split-KV decomposition of the ML-Triton paper, section 3.2 (Flash Decoding splits
+ * the keys and values of long KV sequences; Figure 10 partitions the KV cache and
+ * reduces the partial results): Nq query rows (typically 1) per head attend to all Nk
+ * keys of the head, with no mask.  The keys are cut into `splits` contiguous ranges;
+ * every range yields a partial result (O_s normalised by its own row sum, and its
+ * logsumexp lse_s), and the partials are merged exactly:
+ *
+ *     lse = log sum_s exp(lse_s),     O = sum_s exp(lse_s - lse) * O_s,
+ *
+ * which is the same O and lse as the definition above over all Nk keys.
+ *
+ *   q, o     [B, H, Nq, d] of `dtype`;  k, v  [B, H, Nk, d] of `dtype` (device pointers)
+ *   lse      [B, H, Nq] float32
+ *   splits   number of key ranges; 0 lets the library choose (mha_fwd_splitkv_splits)
+ *   workspace, workspace_bytes
+ *            caller-owned device memory of at least mha_fwd_splitkv_workspace_size(...)
+ *            bytes, 16-byte aligned, holding the float32 partial results; its contents
+ *            are scratch (overwritten, never read before written).  Calls that share a
+ *            workspace must not overlap in time.
+ *   other arguments as for mha_fwd.
+ *
+ * Errors as for mha_fwd, plus MHA_ERR_INVALID_ARG for Nq or Nk < 1, splits < 0, a null
+ * workspace or one smaller than required.  Two kernels are enqueued on `stream`.
+ */
+mha_status mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, float scale, mha_dtype dtype,
+                           int splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* mha_fwd_splitkv_validate -- the argument checks of mha_fwd_splitkv alone, host only. */
+mha_status mha_fwd_splitkv_validate(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, int B, int H, int Nq, int Nk, int d,
+                                    float scale, mha_dtype dtype, int splits,
+                                    const void* workspace, size_t workspace_bytes);
+
+/*
+ * mha_fwd_splitkv_splits -- the number of key ranges mha_fwd_splitkv will use for a
+ * request of `splits` (0: automatic, about 512 workgroups with at least 512 keys per
+ * range).  Every range is a whole number of 64-key tiles.  0 for invalid sizes.
+ */
+int mha_fwd_splitkv_splits(int B, int H, int Nq, int Nk, int splits);
+
+/*
+ * mha_fwd_splitkv_workspace_size -- bytes of workspace mha_fwd_splitkv needs:
+ * resolved_splits * B * H * Nq * (d + 1) * 4.  0 for invalid sizes.  Host only.
+ */
+size_t mha_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int splits);
+
+/*
+ * mha_fwd_splitkv_bytes -- algorithmic HBM traffic of one mha_fwd_splitkv call: Q read
+ * and O written (B*H*Nq*d elements each), K and V read once (B*H*Nk*d each), plus the
+ * float32 LSE (the float32 partials are extra, implementation traffic).  Host only.
+ */
+double mha_fwd_splitkv_bytes(int B, int H, int Nq, int Nk, int d, mha_dtype dtype);
 
 /* mha_status_string -- static, human-readable text for a status code. */
 const char* mha_status_string(mha_status status);

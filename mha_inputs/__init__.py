@@ -26,6 +26,7 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "SWEEP",
+    "DECODE",
     "f32_to_bf16_bits",
     "f32_to_f16_bits",
     "draw",
@@ -71,6 +72,7 @@ class Workload:
     seed: int
     qk_dist: Dist = field(default_factory=lambda: Dist("normal", 1.0))
     v_dist: Dist = field(default_factory=lambda: Dist("normal", 1.0))
+    Nk: int = 0   # keys per head when it differs from the N query rows (split-KV decoding)
 
     @property
     def scale(self) -> float:
@@ -80,9 +82,17 @@ class Workload:
     def shape(self) -> Tuple[int, int, int, int]:
         return (self.B, self.H, self.N, self.d)
 
+    @property
+    def kv_len(self) -> int:
+        return self.Nk or self.N
+
+    @property
+    def kv_shape(self) -> Tuple[int, int, int, int]:
+        return (self.B, self.H, self.kv_len, self.d)
+
     def credited_flops(self) -> float:
-        """4*B*H*N^2*d, halved for the causal mask."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        """4*B*H*N*Nk*d, halved for the causal mask."""
+        f = 4.0 * self.B * self.H * self.N * self.kv_len * self.d
         return f / 2.0 if self.causal else f
 
 
@@ -118,6 +128,21 @@ for _i, (_d, _causal, _N) in enumerate(
     SWEEP[_w.name] = _w
 
 
+# Split-KV decoding: few query rows against a long key/value sequence, no mask.  The
+# pages give no sizes (only that the query length is typically 1): batch x heads x keys
+# are chosen to stream 0.5-1 GiB of K/V per call.
+DECODE: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("bf16_decode_B8_H8_Nk32768_d128", 8, 8, 1, 128, "bf16", False, seed=200, Nk=32768),
+        Workload("bf16_decode_B64_H8_Nk4096_d128", 64, 8, 1, 128, "bf16", False, seed=201, Nk=4096),
+        Workload("bf16_decode_B8_H8_Nk32768_d128_q4", 8, 8, 4, 128, "bf16", False, seed=202, Nk=32768),
+        Workload("bf16_decode_B1_H8_Nk131072_d128", 1, 8, 1, 128, "bf16", False, seed=203, Nk=131072),
+        Workload("f16_decode_B16_H16_Nk8192_d64", 16, 16, 1, 64, "f16", False, seed=204, Nk=8192),
+    ]
+}
+
+
 def _sample(rng: np.random.Generator, shape, dist: Dist) -> np.ndarray:
     if dist.kind == "normal":
         x = rng.standard_normal(size=shape, dtype=np.float32)
@@ -130,8 +155,9 @@ def _sample(rng: np.random.Generator, shape, dist: Dist) -> np.ndarray:
 
 
 def draw(shape, dtype: str, seed: int, qk_dist: Dist = Dist("normal", 1.0),
-         v_dist: Dist = Dist("normal", 1.0)) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Draw Q, K, V of ``shape`` (``[B,H,N,d]``) from ``seed``.
+         v_dist: Dist = Dist("normal", 1.0), kv_shape=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Draw Q of ``shape`` (``[B,H,N,d]``) and K, V of ``kv_shape`` (default ``shape``)
+    from ``seed``.
 
     Returns float32 arrays for ``dtype == "f32"`` and uint16 bit patterns for
     ``dtype == "bf16"`` or ``"f16"``.
@@ -140,9 +166,10 @@ def draw(shape, dtype: str, seed: int, qk_dist: Dist = Dist("normal", 1.0),
         raise ValueError(f"unknown dtype {dtype!r}")
     children = np.random.SeedSequence(seed).spawn(3)
     out = []
-    for child, dist in zip(children, (qk_dist, qk_dist, v_dist)):
+    shapes = (shape, kv_shape or shape, kv_shape or shape)
+    for child, dist, shp in zip(children, (qk_dist, qk_dist, v_dist), shapes):
         rng = np.random.Generator(np.random.PCG64(child))
-        x = _sample(rng, shape, dist)
+        x = _sample(rng, shp, dist)
         if dtype == "bf16":
             x = f32_to_bf16_bits(x)
         elif dtype == "f16":
@@ -153,4 +180,4 @@ def draw(shape, dtype: str, seed: int, qk_dist: Dist = Dist("normal", 1.0),
 
 def draw_qkv(w: Workload):
     """Q, K, V for one of the named workloads."""
-    return draw(w.shape, w.dtype, w.seed, w.qk_dist, w.v_dist)
+    return draw(w.shape, w.dtype, w.seed, w.qk_dist, w.v_dist, w.kv_shape if w.Nk else None)

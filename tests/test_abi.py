@@ -94,3 +94,46 @@ def test_python_wrapper_checks_shapes_on_cpu():
         mha.fwd(q, q, q)                    # CPU tensors are refused before any call
     with pytest.raises(ValueError):
         mha.fwd(q[0], q[0], q[0])           # wrong rank
+
+
+def sv(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, Nq=1, Nk=1000, d=128, scale=0.1, dtype=BF16,
+             splits=0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return mha.mha_fwd_splitkv_validate(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                        a["Nq"], a["Nk"], a["d"], a["scale"], a["dtype"], a["splits"],
+                                        a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(dtype=F32, d=64), OK), (dict(dtype=F16, splits=5), OK),
+    (dict(ws=0), INVALID), (dict(wsb=16), INVALID), (dict(Nq=0), INVALID), (dict(Nk=0), INVALID),
+    (dict(splits=-1), INVALID), (dict(q=0), INVALID), (dict(dtype=3), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(d=96), UNSUPPORTED), (dict(ws=P + 4), UNSUPPORTED),
+    (dict(k=P + 8), UNSUPPORTED),
+])
+def test_splitkv_validate(kw, code):
+    assert sv(**kw) == code
+
+
+def test_splitkv_rejects_before_launch():
+    assert mha.mha_fwd_splitkv(P, P, P, P, P, 1, 1, 1, 100, 64, 0.1, BF16, 0, 0, 0, 0) == INVALID
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 1, 1, 1), (1, 32, 1, 16384), (16, 32, 1, 16384), (1, 8, 4, 131072),
+                                        (3, 5, 130, 999), (64, 8, 1, 4096), (1, 1, 1, 100)])
+@pytest.mark.parametrize("splits", [0, 1, 2, 7, 1000])
+def test_splitkv_partition(B, H, Nq, Nk, splits):
+    s = mha.mha_fwd_splitkv_splits(B, H, Nq, Nk, splits)
+    tiles = -(-Nk // 64)
+    assert 1 <= s <= tiles
+    if splits > 0:
+        assert s <= splits
+    else:
+        # about 512 workgroups, at least 512 keys per range (unless one range)
+        blocks = -(-Nq // 128) * B * H
+        assert s == 1 or (s - 1) * 512 < Nk
+        assert s <= max(1, -(-512 // blocks))
+    assert mha.mha_fwd_splitkv_workspace_size(B, H, Nq, Nk, 128, splits) == s * B * H * Nq * 129 * 4
+    assert mha.mha_fwd_splitkv_bytes(B, H, Nq, Nk, 128, BF16) == \
+        (2 * Nq + 2 * Nk) * B * H * 128 * 2 + 4 * B * H * Nq

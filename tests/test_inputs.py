@@ -67,3 +67,12 @@ def test_pages_sweep_table():
     assert len({w.seed for w in mi.SWEEP.values()}) == 24
     q = mi.draw((1, 1, 8, 8), "f16", 3)[0]
     assert q.dtype == np.uint16
+
+
+def test_decode_table_and_kv_shapes():
+    for w in mi.DECODE.values():
+        assert w.Nk > w.N and not w.causal and w.kv_shape == (w.B, w.H, w.Nk, w.d)
+        assert w.credited_flops() == 4.0 * w.B * w.H * w.N * w.Nk * w.d
+    assert len({w.seed for w in mi.DECODE.values()}) == len(mi.DECODE)
+    q, k, v = mi.draw((1, 2, 3, 8), "bf16", 5, kv_shape=(1, 2, 40, 8))
+    assert q.shape == (1, 2, 3, 8) and k.shape == v.shape == (1, 2, 40, 8)

@@ -87,3 +87,35 @@ def test_causal_requires_square():
     q, k, v = pins.rand_qkv(1, 1, 1, 4, 4, Nk=5)
     with pytest.raises(ValueError):
         oracle.attention_forward(q, k, v, causal=True, scale=1.0)
+
+
+def test_bruteforce_decimal_nonsquare():
+    # fewer query rows than keys (split-KV decoding): the definition over all keys
+    for n, (B, H, Nq, Nk, d) in enumerate([(1, 1, 1, 9, 4), (1, 2, 3, 17, 5), (2, 1, 2, 1, 3)]):
+        q, k, v = pins.rand_qkv(300 + n, B, H, Nq, d, sigma=1.5, Nk=Nk)
+        O, L = oracle.attention_forward(q, k, v, causal=False, scale=0.6)
+        Ob, Lb = pins.decimal_attention(q, k, v, False, 0.6)
+        assert np.max(np.abs(O - Ob)) <= 1e-12 and np.max(np.abs(L - Lb)) <= 1e-12
+
+
+def test_nonsquare_closed_forms():
+    # Q = 0: every key has weight 1/Nk, so O is the mean of V and lse = ln Nk
+    q, k, v = pins.rand_qkv(7, 2, 3, 4, 8, Nk=300)
+    O, L = oracle.attention_forward(np.zeros_like(q), k, v, causal=False, scale=0.3)
+    assert np.max(np.abs(O - v.mean(axis=2, keepdims=True))) <= 1e-12
+    assert np.max(np.abs(L - np.log(300))) <= 1e-12
+
+
+def test_split_merge_identity():
+    # Partial results over disjoint key ranges merge exactly into the full result:
+    # lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s (the split-KV merge)
+    q, k, v = pins.rand_qkv(8, 2, 2, 3, 16, sigma=2.0, Nk=1000)
+    O, L = oracle.attention_forward(q, k, v, causal=False, scale=0.4)
+    for bounds in ([0, 1000], [0, 1, 1000], [0, 64, 500, 999, 1000], list(range(0, 1001, 125))):
+        parts = [oracle.attention_forward(q, k[:, :, a:b], v[:, :, a:b], causal=False, scale=0.4)
+                 for a, b in zip(bounds[:-1], bounds[1:])]
+        lse_s = np.stack([p_[1] for p_ in parts])
+        m = lse_s.max(axis=0)
+        lse = m + np.log(np.exp(lse_s - m).sum(axis=0))
+        om = sum(np.exp(p_[1] - lse)[..., None] * p_[0] for p_ in parts)
+        assert np.max(np.abs(lse - L)) <= 1e-12 and np.max(np.abs(om - O)) <= 1e-12
