@@ -541,24 +541,56 @@ hipError_t launch(const Params& p, hipStream_t stream) {
 
 // Merge of the split-KV partial results (the cross-partition reduction of split-KV
 // decoding): for one query row with partials (O_s, lse_s), s = 0..S-1,
-//   lse = M + ln(sum_s exp(lse_s - M)),  M = max_s lse_s,
-//   O   = sum_s exp(lse_s - lse) * O_s.
-// One workgroup of D threads per row; thread c produces column c.
+//   lse = M + ln L,  M = max_s lse_s,  L = sum_s exp(lse_s - M),
+//   O   = sum_s w_s * O_s,  w_s = exp(lse_s - M) / L.
+// One workgroup of kMergeThreads per row: M and L are block reductions over the splits,
+// the weights go to LDS, then thread c forms column c.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeLdsWeights = 2048;
+
+__device__ __forceinline__ float block_reduce(float x, float* red, bool is_max) {
+  red[threadIdx.x] = x;
+  __syncthreads();
+  for (int off = kMergeThreads / 2; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) {
+      const float y = red[threadIdx.x + off];
+      red[threadIdx.x] = is_max ? fmaxf(red[threadIdx.x], y) : red[threadIdx.x] + y;
+    }
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(D) void mha_merge_kernel(Params p) {
+__global__ __launch_bounds__(kMergeThreads) void mha_merge_kernel(Params p) {
+  __shared__ float red[kMergeThreads];
+  __shared__ float wts[kMergeLdsWeights];
   const size_t row = blockIdx.x;                      // (b*H + h) * N + query row
   const size_t stride = (size_t)p.BH * (size_t)p.N;   // between splits
-  const int c = threadIdx.x;
+  const int t = threadIdx.x;
   float m = -__builtin_inff();
-  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_lse[s * stride + row]);
-  float wsum = 0.f, o = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float w = __builtin_amdgcn_exp2f((p.part_lse[s * stride + row] - m) * kLog2e);
-    wsum += w;
-    o += w * p.part_o[(s * stride + row) * D + c];
+  for (int s = t; s < p.splits; s += kMergeThreads) m = fmaxf(m, p.part_lse[s * stride + row]);
+  const float M = block_reduce(m, red, true);
+  float sum = 0.f;
+  for (int s = t; s < p.splits; s += kMergeThreads) {
+    const float e = __builtin_amdgcn_exp2f((p.part_lse[s * stride + row] - M) * kLog2e);
+    sum += e;
+    if (s < kMergeLdsWeights) wts[s] = e;
   }
-  ((T*)p.o)[row * D + c] = (T)(o / wsum);
-  if (c == 0) p.lse[row] = m + __builtin_amdgcn_logf(wsum) * kLn2;
+  const float L = block_reduce(sum, red, false);     // also orders the wts writes
+  const float invL = 1.0f / L;
+  for (int c = t; c < D; c += kMergeThreads) {
+    float o = 0.f;
+    for (int s = 0; s < p.splits; ++s) {
+      const float w = s < kMergeLdsWeights ? wts[s]
+                                           : __builtin_amdgcn_exp2f((p.part_lse[s * stride + row] - M) * kLog2e);
+      o += w * p.part_o[(s * stride + row) * D + c];
+    }
+    ((T*)p.o)[row * D + c] = (T)(o * invL);
+  }
+  if (t == 0) p.lse[row] = M + __builtin_amdgcn_logf(L) * kLn2;
 }
 
 template <typename T, int D>
@@ -566,7 +598,7 @@ hipError_t launch_split(const Params& p, hipStream_t stream) {
   hipLaunchKernelGGL((mha_fwd_kernel<T, D, false, true>), dim3(p.total), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mha_merge_kernel<T, D>), dim3(p.BH * p.N), dim3(D), 0, stream, p);
+  hipLaunchKernelGGL((mha_merge_kernel<T, D>), dim3(p.BH * p.N), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
