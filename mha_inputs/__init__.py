@@ -27,10 +27,15 @@ __all__ = [
     "WORKLOADS",
     "SWEEP",
     "DECODE",
+    "PagedWorkload",
+    "PAGED",
     "f32_to_bf16_bits",
     "f32_to_f16_bits",
     "draw",
     "draw_qkv",
+    "draw_paged",
+    "draw_paged_workload",
+    "paged_lengths",
 ]
 
 
@@ -143,6 +148,49 @@ DECODE: Dict[str, Workload] = {
 }
 
 
+@dataclass(frozen=True)
+class PagedWorkload:
+    """Decoding against a paged key/value cache.
+
+    ``B`` sequences of ``H`` heads, ``Nq`` query rows each; sequence lengths drawn
+    uniformly from ``[len_lo, len_hi]`` (or all equal when ``len_lo == len_hi``);
+    blocks of ``block_size`` keys; the pool holds the used blocks plus ``spare``
+    unused ones.  See :func:`draw_paged`.
+    """
+
+    name: str
+    B: int
+    H: int
+    Nq: int
+    d: int
+    dtype: str
+    block_size: int
+    len_lo: int
+    len_hi: int
+    seed: int
+    spare: int = 16
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+
+# Paged decoding.  The pages give neither sizes nor a block size: a serving-style mix of
+# sequence lengths with the small blocks of paged KV caches (16 keys), a long-context
+# case with large blocks, the contiguous split-KV decoding shape with 256-key blocks (the
+# cost of the indirection), and an fp16 d=64 case with several query rows.
+PAGED: Dict[str, PagedWorkload] = {
+    w.name: w
+    for w in [
+        PagedWorkload("bf16_paged_B64_H8_d128_bs16_len512-8192", 64, 8, 1, 128, "bf16", 16, 512, 8192, seed=300),
+        PagedWorkload("bf16_paged_B16_H32_d128_bs64_len1024-16384", 16, 32, 1, 128, "bf16", 64, 1024, 16384,
+                      seed=301),
+        PagedWorkload("bf16_paged_B8_H8_d128_bs256_len32768", 8, 8, 1, 128, "bf16", 256, 32768, 32768, seed=302),
+        PagedWorkload("f16_paged_B32_H16_d64_bs32_q4_len256-4096", 32, 16, 4, 64, "f16", 32, 256, 4096, seed=303),
+    ]
+}
+
+
 def _sample(rng: np.random.Generator, shape, dist: Dist) -> np.ndarray:
     if dist.kind == "normal":
         x = rng.standard_normal(size=shape, dtype=np.float32)
@@ -181,3 +229,47 @@ def draw(shape, dtype: str, seed: int, qk_dist: Dist = Dist("normal", 1.0),
 def draw_qkv(w: Workload):
     """Q, K, V for one of the named workloads."""
     return draw(w.shape, w.dtype, w.seed, w.qk_dist, w.v_dist, w.kv_shape if w.Nk else None)
+
+
+def draw_paged(B: int, H: int, Nq: int, d: int, dtype: str, block_size: int, seq_lens, seed: int,
+               spare: int = 16, dist: Dist = Dist("normal", 1.0)):
+    """Q and a paged K/V cache from ``seed``.
+
+    ``seq_lens``: ``B`` key counts.  Every sequence gets ``ceil(len / block_size)``
+    physical blocks; the pool holds those plus ``spare`` more, and the physical block
+    ids are a seeded random permutation, so the blocks of one sequence are scattered
+    over the pool.  Table entries past a sequence's last block are -1.  Returns
+    ``(q [B,H,Nq,d], k_pool, v_pool [num_blocks,H,block_size,d], block_table
+    [B, max_blocks] int32, seq_lens [B] int32)``, values encoded as for :func:`draw`
+    (the unused rows of the pool hold draws too).
+    """
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    if lens.shape != (B,) or (lens < 0).any():
+        raise ValueError("need B non-negative sequence lengths")
+    per_seq = (lens + block_size - 1) // block_size
+    max_blocks = max(1, int(per_seq.max()))
+    num_blocks = int(per_seq.sum()) + int(spare)
+    if num_blocks < 1:
+        raise ValueError("empty pool")
+    children = np.random.SeedSequence(seed).spawn(4)
+    perm = np.random.Generator(np.random.PCG64(children[0])).permutation(num_blocks)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    at = 0
+    for b in range(B):
+        n = int(per_seq[b])
+        table[b, :n] = perm[at:at + n]
+        at += n
+    pool_shape = (num_blocks, H, block_size, d)
+    q, k, v = draw((B, H, Nq, d), dtype, int(children[1].generate_state(1)[0]), dist, dist, kv_shape=pool_shape)
+    return q, k, v, table, lens.astype(np.int32)
+
+
+def paged_lengths(w: PagedWorkload) -> np.ndarray:
+    """The sequence lengths of a paged workload (seeded, uniform in [len_lo, len_hi])."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(w.seed).spawn(1)[0]))
+    return rng.integers(w.len_lo, w.len_hi + 1, size=w.B).astype(np.int64)
+
+
+def draw_paged_workload(w: PagedWorkload):
+    """Inputs of a named paged workload (see :func:`draw_paged`)."""
+    return draw_paged(w.B, w.H, w.Nq, w.d, w.dtype, w.block_size, paged_lengths(w), w.seed + 1, w.spare)

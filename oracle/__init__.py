@@ -10,7 +10,9 @@ Contents:
     in float64 (what the fused kernel must reproduce up to rounding);
   * :mod:`oracle.online` -- the tiled online-softmax recurrence in float64, step for
     step as the FlashAttention-2 algorithm states it, used to check readings of the
-    algorithm (deferred normalisation, masked tiles) on the CPU.
+    algorithm (deferred normalisation, masked tiles) on the CPU;
+  * :mod:`oracle.paged` -- attention over a paged key/value cache (keys reached
+    through a block table), the plain definition applied to the gathered keys.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against brute force in
 40-digit decimal arithmetic, a library attention routine in float64, closed forms
@@ -22,3 +24,4 @@ from .attention import (  # noqa: F401
     attention_rows,
 )
 from .online import attention_forward_tiled  # noqa: F401
+from .paged import gather_keys, paged_attention_forward  # noqa: F401

@@ -76,3 +76,27 @@ def test_decode_table_and_kv_shapes():
     assert len({w.seed for w in mi.DECODE.values()}) == len(mi.DECODE)
     q, k, v = mi.draw((1, 2, 3, 8), "bf16", 5, kv_shape=(1, 2, 40, 8))
     assert q.shape == (1, 2, 3, 8) and k.shape == v.shape == (1, 2, 40, 8)
+
+
+def test_draw_paged_scatters_each_block_once():
+    lens = [0, 1, 16, 17, 100]
+    q, kp, vp, table, sl = mi.draw_paged(5, 3, 2, 64, "bf16", 16, lens, seed=11, spare=4)
+    per = [-(-L // 16) for L in lens]
+    assert q.shape == (5, 3, 2, 64) and kp.shape == vp.shape == (sum(per) + 4, 3, 16, 64)
+    assert table.dtype == np.int32 and sl.dtype == np.int32 and list(sl) == lens
+    assert table.shape == (5, max(per))
+    used = np.concatenate([table[b, :c] for b, c in enumerate(per)])
+    assert len(set(used.tolist())) == len(used) and used.min() >= 0 and used.max() < kp.shape[0]
+    for b, c in enumerate(per):
+        assert np.all(table[b, c:] == -1)
+    again = mi.draw_paged(5, 3, 2, 64, "bf16", 16, lens, seed=11, spare=4)
+    for x, y in zip((q, kp, vp, table, sl), again):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_paged_workloads():
+    for name, w in mi.PAGED.items():
+        lens = mi.paged_lengths(w)
+        assert lens.shape == (w.B,) and lens.min() >= w.len_lo and lens.max() <= w.len_hi, name
+        assert w.block_size & (w.block_size - 1) == 0 and w.block_size >= 16, name
+        assert name.startswith(w.dtype) and f"_bs{w.block_size}_" in name, name
