@@ -119,6 +119,59 @@ def time_gpu_splitkv(w, steps, warmup, dev):
     return dict(total_ms=ev[0].elapsed_time(ev[steps]), inputs=(q, k, v), out=(o, lse))
 
 
+def time_gpu_paged(w, steps, warmup, dev, splits=0):
+    """As time_gpu, for the paged split-KV forward of a paged workload."""
+    import torch
+
+    import head_attention_fa2_amd as mha
+    import mha_inputs
+
+    q, kp, vp, table, lens = mha_inputs.draw_paged_workload(w)
+    tq, tk, tv = (_to_device(x, w.dtype, dev) for x in (q, kp, vp))
+    tt, tl = torch.from_numpy(table).to(dev), torch.from_numpy(lens).to(dev)
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(mha.mha_fwd_paged_workspace_size(w.B, w.H, w.Nq, w.d, w.block_size, table.shape[1], splits),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        mha.fwd_paged(tq, tk, tv, tt, tl, scale=w.scale, splits=splits, out=o, lse=lse, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize(dev)
+    return dict(total_ms=ev[0].elapsed_time(ev[1]), inputs=(q, kp, vp, table, lens), out=(o, lse))
+
+
+def parity_sample_paged(w, inputs, out, n=6):
+    """Max abs error of sampled output rows of a paged workload against the CPU oracle."""
+    import numpy as np
+
+    import oracle
+
+    q, kp, vp, table, lens = inputs
+    o, lse = out
+    rng = np.random.default_rng(w.seed + 1)
+    eo = el = 0.0
+    for _ in range(n):
+        b, h, i = int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.Nq))
+        c = -(-int(lens[b]) // w.block_size)
+        used = table[b, :c]
+        ob, lb = oracle.paged_attention_forward(
+            oracle.decode(q[b:b + 1, h:h + 1, i:i + 1], w.dtype), oracle.decode(kp[used, h:h + 1], w.dtype),
+            oracle.decode(vp[used, h:h + 1], w.dtype), np.arange(c)[None], lens[b:b + 1], scale=w.scale)
+        eo = max(eo, float(np.max(np.abs(o[b, h, i].float().cpu().numpy() - ob[0, 0, 0]))))
+        el = max(el, abs(float(lse[b, h, i]) - float(lb[0, 0, 0])))
+    return {"max_abs_dO": eo, "max_abs_dLSE": el, "rows": n}
+
+
 def parity_sample(w, inputs, out, n=24):
     """Max abs error of sampled output rows against the CPU oracle."""
     import numpy as np
@@ -185,6 +238,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time every workload (lines on stderr)")
     ap.add_argument("--decode", action="store_true",
                     help="also time the split-KV decode workloads (lines on stderr)")
+    ap.add_argument("--paged", action="store_true",
+                    help="also time the paged split-KV decode workloads (lines on stderr)")
     ap.add_argument("--pages-sweep", action="store_true",
                     help="also time the fp16 sweep of the paper's FlashAttention-2 figures (lines on stderr)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -273,6 +328,23 @@ def main():
                               "pct_of_hbm": round(100 * nbytes / (m * 1e-3) / 1e9 / HBM_GBS, 2),
                               "TFLOP/s": round(ww.credited_flops() / (m * 1e-3) / 1e12, 2),
                               "parity": parity_sample(ww, rr["inputs"], rr["out"], n=8)}),
+                  file=sys.stderr, flush=True)
+            del rr
+    if args.paged:
+        for name, ww in mha_inputs.PAGED.items():
+            steps = max(10, args.steps // 2)
+            rr = time_gpu_paged(ww, steps, 10, dev)
+            m = rr["total_ms"] / steps
+            table, lens = rr["inputs"][3], rr["inputs"][4]
+            total_keys = int(lens.sum())
+            nbytes = mha.mha_fwd_paged_bytes(ww.B, ww.H, ww.Nq, total_keys, ww.d,
+                                             {"f32": 0, "bf16": 1, "f16": 2}[ww.dtype])
+            print(json.dumps({"workload": name, "B": ww.B, "H": ww.H, "Nq": ww.Nq, "d": ww.d,
+                              "block_size": ww.block_size, "total_keys": total_keys,
+                              "splits": mha.mha_fwd_paged_splits(ww.B, ww.H, ww.Nq, ww.block_size, table.shape[1], 0),
+                              "ms": round(m, 5), "GB/s": round(nbytes / (m * 1e-3) / 1e9, 1),
+                              "pct_of_hbm": round(100 * nbytes / (m * 1e-3) / 1e9 / HBM_GBS, 2),
+                              "parity": parity_sample_paged(ww, rr["inputs"], rr["out"])}),
                   file=sys.stderr, flush=True)
             del rr
     if args.pages_sweep:

@@ -4,9 +4,11 @@ The compute is entirely in ``libmha.so`` (hand-written HIP kernels for gfx950 be
 the C ABI of ``include/mha.h``).  This module only marshals arguments: the functions
 ``mha_fwd``, ``mha_fwd_validate``, ``mha_fwd_flops``, ``mha_fwd_bytes``,
 ``mha_fwd_splitkv``, ``mha_fwd_splitkv_validate``, ``mha_fwd_splitkv_splits``,
-``mha_fwd_splitkv_workspace_size``, ``mha_fwd_splitkv_bytes``, ``mha_status_string``
-and ``mha_version`` mirror the C entry points one to one, and :func:`fwd` /
-:func:`fwd_splitkv` are the PyTorch-facing conveniences (device memory and the stream
+``mha_fwd_splitkv_workspace_size``, ``mha_fwd_splitkv_bytes``, ``mha_fwd_paged``,
+``mha_fwd_paged_validate``, ``mha_fwd_paged_splits``, ``mha_fwd_paged_workspace_size``,
+``mha_fwd_paged_bytes``, ``mha_status_string`` and ``mha_version`` mirror the C entry
+points one to one, and :func:`fwd` / :func:`fwd_splitkv` / :func:`fwd_paged` are the
+PyTorch-facing conveniences (device memory and the stream
 come from torch; nothing is computed in Python).  There is no fallback: if the library is not
 built or a call fails, an exception is raised.
 """
@@ -21,8 +23,9 @@ __all__ = [
     "MHA_DTYPE_F32", "MHA_DTYPE_BF16", "MHA_DTYPE_F16",
     "library_path", "load", "mha_fwd", "mha_fwd_validate", "mha_fwd_flops",
     "mha_fwd_bytes", "mha_fwd_splitkv", "mha_fwd_splitkv_validate", "mha_fwd_splitkv_splits",
-    "mha_fwd_splitkv_workspace_size", "mha_fwd_splitkv_bytes", "mha_status_string", "mha_version",
-    "fwd", "fwd_splitkv", "MhaError",
+    "mha_fwd_splitkv_workspace_size", "mha_fwd_splitkv_bytes", "mha_fwd_paged", "mha_fwd_paged_validate",
+    "mha_fwd_paged_splits", "mha_fwd_paged_workspace_size", "mha_fwd_paged_bytes", "mha_status_string",
+    "mha_version", "fwd", "fwd_splitkv", "fwd_paged", "MhaError",
 ]
 
 MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_HIP = 0, 1, 2, 3
@@ -73,6 +76,16 @@ def load() -> ctypes.CDLL:
     lib.mha_fwd_splitkv_workspace_size.restype = sz
     lib.mha_fwd_splitkv_bytes.argtypes = [i, i, i, i, i, i]
     lib.mha_fwd_splitkv_bytes.restype = ctypes.c_double
+    lib.mha_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.mha_fwd_paged.restype = i
+    lib.mha_fwd_paged_validate.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz]
+    lib.mha_fwd_paged_validate.restype = i
+    lib.mha_fwd_paged_splits.argtypes = [i, i, i, i, i, i]
+    lib.mha_fwd_paged_splits.restype = i
+    lib.mha_fwd_paged_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.mha_fwd_paged_workspace_size.restype = sz
+    lib.mha_fwd_paged_bytes.argtypes = [i, i, i, ctypes.c_longlong, i, i]
+    lib.mha_fwd_paged_bytes.restype = ctypes.c_double
     lib.mha_status_string.argtypes = [i]
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_version.argtypes = []
@@ -126,6 +139,38 @@ def mha_fwd_splitkv_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, spl
 
 def mha_fwd_splitkv_bytes(B: int, H: int, Nq: int, Nk: int, d: int, dtype: int) -> float:
     return load().mha_fwd_splitkv_bytes(B, H, Nq, Nk, d, dtype)
+
+
+def mha_fwd_paged(q: int, k_pool: int, v_pool: int, block_table: int, seq_lens: int, o: int, lse: int,
+                  B: int, H: int, Nq: int, d: int, num_blocks: int, block_size: int, max_blocks: int,
+                  scale: float, dtype: int, splits: int, workspace: int, workspace_bytes: int,
+                  stream: int) -> int:
+    """Enqueue the paged split-KV forward (partials, then the merge) on ``stream``."""
+    return load().mha_fwd_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H, Nq, d, num_blocks,
+                                block_size, max_blocks, scale, dtype, splits, workspace, workspace_bytes,
+                                stream)
+
+
+def mha_fwd_paged_validate(q: int, k_pool: int, v_pool: int, block_table: int, seq_lens: int, o: int,
+                           lse: int, B: int, H: int, Nq: int, d: int, num_blocks: int, block_size: int,
+                           max_blocks: int, scale: float, dtype: int, splits: int, workspace: int,
+                           workspace_bytes: int) -> int:
+    return load().mha_fwd_paged_validate(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H, Nq, d,
+                                         num_blocks, block_size, max_blocks, scale, dtype, splits, workspace,
+                                         workspace_bytes)
+
+
+def mha_fwd_paged_splits(B: int, H: int, Nq: int, block_size: int, max_blocks: int, splits: int) -> int:
+    return load().mha_fwd_paged_splits(B, H, Nq, block_size, max_blocks, splits)
+
+
+def mha_fwd_paged_workspace_size(B: int, H: int, Nq: int, d: int, block_size: int, max_blocks: int,
+                                 splits: int) -> int:
+    return load().mha_fwd_paged_workspace_size(B, H, Nq, d, block_size, max_blocks, splits)
+
+
+def mha_fwd_paged_bytes(B: int, H: int, Nq: int, total_keys: int, d: int, dtype: int) -> float:
+    return load().mha_fwd_paged_bytes(B, H, Nq, total_keys, d, dtype)
 
 
 def mha_status_string(status: int) -> str:
@@ -225,6 +270,63 @@ def fwd_splitkv(q, k, v, scale: Optional[float] = None, splits: int = 0, out=Non
                          B, H, Nq, Nk, d, float(scale), _DTYPES[q.dtype], int(splits),
                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                          stream.cuda_stream)
+    if st != MHA_OK:
+        raise MhaError(st)
+    return out, lse
+
+
+def fwd_paged(q, k_pool, v_pool, block_table, seq_lens, scale: Optional[float] = None, splits: int = 0,
+              out=None, lse=None, workspace=None, stream=None) -> Tuple["object", "object"]:
+    """``O, LSE = fwd_paged(q, k_pool, v_pool, block_table, seq_lens)``: ``q``
+    ``[B, H, Nq, d]`` against the keys of a paged cache, ``k_pool, v_pool``
+    ``[num_blocks, H, block_size, d]`` (one dtype with q), ``block_table`` int32
+    ``[B, max_blocks]`` and ``seq_lens`` int32 ``[B]``, all contiguous on one GPU.  Key j
+    of sequence b is row ``j % block_size`` of block ``block_table[b, j // block_size]``.
+    ``workspace`` as for :func:`fwd_splitkv` (size :func:`mha_fwd_paged_workspace_size`).
+    Enqueued on ``stream`` (default: torch's current stream); no sync.
+    """
+    import torch
+
+    _DTYPES = {torch.float32: MHA_DTYPE_F32, torch.bfloat16: MHA_DTYPE_BF16, torch.float16: MHA_DTYPE_F16}
+    if q.dim() != 4 or k_pool.dim() != 4 or v_pool.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and the pools [num_blocks, H, block_size, d]")
+    B, H, Nq, d = q.shape
+    num_blocks, _, block_size, _ = k_pool.shape
+    if k_pool.shape != (num_blocks, H, block_size, d) or v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool must be [num_blocks, H, block_size, d] with the heads and d of q")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    tensors = (q, k_pool, v_pool, block_table, seq_lens)
+    if not all(t.is_cuda for t in tensors) or len({t.device for t in tensors}) != 1:
+        raise ValueError("all inputs must be on the same GPU")
+    if q.dtype not in _DTYPES or k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise ValueError("q and the pools must all be float32, all bfloat16 or all float16")
+    if not all(t.is_contiguous() for t in tensors):
+        raise ValueError("all inputs must be contiguous")
+    max_blocks = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    need = mha_fwd_paged_workspace_size(B, H, Nq, d, block_size, max_blocks, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = mha_fwd_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+                       seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, d, num_blocks,
+                       block_size, max_blocks, float(scale), _DTYPES[q.dtype], int(splits),
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream.cuda_stream)
     if st != MHA_OK:
         raise MhaError(st)
     return out, lse

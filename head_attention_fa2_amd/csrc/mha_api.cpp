@@ -52,6 +52,14 @@ Partition partition(int B, int H, int Nq, int Nk, int splits) {
   return Partition{(int)(((int64_t)Nk + chunk - 1) / chunk), (int)chunk};
 }
 
+// Paged: the automatic choice is the split-KV one over the longest possible sequence
+// (max_blocks * block_size keys).  Measured on the paged decoding workloads (lengths
+// 256..16384, 512 and more heads x sequences), one range per sequence beat 2, 4, 8 and 16:
+// short sequences finish early and the long ones then get more of the bandwidth.
+Partition partition_paged(int B, int H, int Nq, int max_keys, int splits) {
+  return partition(B, H, Nq, max_keys, splits);
+}
+
 size_t workspace_bytes(int B, int H, int Nq, int d, int splits) {
   return (size_t)splits * (size_t)B * (size_t)H * (size_t)Nq * ((size_t)d + 1) * sizeof(float);
 }
@@ -72,6 +80,41 @@ mha_status validate_splitkv(const void* q, const void* k, const void* v, const v
   const int64_t bm = mha_impl::fwd_query_block((int)dtype);
   const int64_t blocks = ((int64_t)Nq + bm - 1) / bm * (int64_t)B * (int64_t)H * pt.splits;
   if (blocks > INT32_MAX || (int64_t)B * H * Nq > INT32_MAX) return MHA_ERR_UNSUPPORTED;
+  return MHA_OK;
+}
+
+// Paged K/V: block size a power of two in [16, 65536]; the key range of every sequence
+// is at most max_blocks * block_size keys, which sizes the partition and workspace.
+int block_size_log2(int block_size) {
+  if (block_size < 16 || block_size > 65536 || (block_size & (block_size - 1)) != 0) return -1;
+  int l = 0;
+  while ((1 << l) < block_size) ++l;
+  return l;
+}
+
+mha_status validate_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, const void* o, const float* lse, int B, int H, int Nq, int d,
+                          int num_blocks, int block_size, int max_blocks, float scale, mha_dtype dtype, int splits,
+                          const void* workspace, size_t ws_bytes) {
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o || !lse || !workspace)
+    return MHA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || num_blocks < 1 || max_blocks < 1 || splits < 0) return MHA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MHA_ERR_INVALID_ARG;
+  if (dtype != MHA_DTYPE_F32 && dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_F16) return MHA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return MHA_ERR_UNSUPPORTED;
+  if (block_size_log2(block_size) < 0) return MHA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0)
+    return MHA_ERR_UNSUPPORTED;
+  const int64_t max_keys = (int64_t)max_blocks * block_size;
+  if (max_keys > (int64_t)1 << 30) return MHA_ERR_UNSUPPORTED;
+  const Partition pt = partition_paged(B, H, Nq, (int)max_keys, splits);
+  if (ws_bytes < workspace_bytes(B, H, Nq, d, pt.splits)) return MHA_ERR_INVALID_ARG;
+  const int64_t bm = mha_impl::fwd_query_block((int)dtype);
+  const int64_t blocks = ((int64_t)Nq + bm - 1) / bm * (int64_t)B * (int64_t)H * pt.splits;
+  if (blocks > INT32_MAX || (int64_t)B * H * Nq > INT32_MAX || (int64_t)B * max_blocks > INT32_MAX)
+    return MHA_ERR_UNSUPPORTED;
   return MHA_OK;
 }
 
@@ -123,6 +166,49 @@ mha_status mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   const hipError_t e = mha_impl::launch_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, (int)dtype, pt.splits,
                                                     pt.chunk, part_o, part_lse, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+mha_status mha_fwd_paged_validate(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens, const void* o,
+                                  const float* lse, int B, int H, int Nq, int d, int num_blocks, int block_size,
+                                  int max_blocks, float scale, mha_dtype dtype, int splits, const void* workspace,
+                                  size_t workspace_bytes) {
+  return validate_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H, Nq, d, num_blocks, block_size,
+                        max_blocks, scale, dtype, splits, workspace, workspace_bytes);
+}
+
+mha_status mha_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                         const int32_t* seq_lens, void* o, float* lse, int B, int H, int Nq, int d, int num_blocks,
+                         int block_size, int max_blocks, float scale, mha_dtype dtype, int splits, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const mha_status st = validate_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H, Nq, d, num_blocks,
+                                       block_size, max_blocks, scale, dtype, splits, workspace, workspace_bytes);
+  if (st != MHA_OK) return st;
+  const Partition pt = partition_paged(B, H, Nq, max_blocks * block_size, splits);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = part_o + (size_t)pt.splits * B * H * Nq * d;
+  const hipError_t e = mha_impl::launch_fwd_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H, Nq, d,
+                                                  scale, (int)dtype, num_blocks, block_size_log2(block_size),
+                                                  max_blocks, pt.splits, pt.chunk, part_o, part_lse,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+int mha_fwd_paged_splits(int B, int H, int Nq, int block_size, int max_blocks, int splits) {
+  if (B < 1 || H < 1 || Nq < 1 || max_blocks < 1 || splits < 0 || block_size_log2(block_size) < 0) return 0;
+  if ((int64_t)max_blocks * block_size > (int64_t)1 << 30) return 0;
+  return partition_paged(B, H, Nq, max_blocks * block_size, splits).splits;
+}
+
+size_t mha_fwd_paged_workspace_size(int B, int H, int Nq, int d, int block_size, int max_blocks, int splits) {
+  const int s = mha_fwd_paged_splits(B, H, Nq, block_size, max_blocks, splits);
+  if (s == 0 || d < 1) return 0;
+  return workspace_bytes(B, H, Nq, d, s);
+}
+
+double mha_fwd_paged_bytes(int B, int H, int Nq, long long total_keys, int d, mha_dtype dtype) {
+  const double elem = dtype == MHA_DTYPE_F32 ? 4.0 : 2.0;
+  return (2.0 * B * Nq + 2.0 * (double)total_keys) * H * (double)d * elem + 4.0 * B * H * (double)Nq;
 }
 
 double mha_fwd_splitkv_bytes(int B, int H, int Nq, int Nk, int d, mha_dtype dtype) {

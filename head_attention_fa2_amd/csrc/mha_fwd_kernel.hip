@@ -111,6 +111,14 @@ struct Params {
   int BH;
   float* part_o;
   float* part_lse;
+  // paged K/V only: heads, block table [B][max_blocks] and key counts [B] (int32), pool
+  // size in blocks, log2 of the block size (keys per block)
+  int H = 0;
+  const int* block_table = nullptr;
+  const int* seq_lens = nullptr;  // also tells the merge that key counts vary per sequence
+  int max_blocks = 0;
+  int num_blocks = 0;
+  int bs_log2 = 0;
 };
 
 // ---------------------------------------------------------------------------- LDS layout
@@ -154,6 +162,23 @@ __device__ __forceinline__ void copy_to_lds(const void* sbase, unsigned voff, un
                : "memory", "m0");
 }
 
+// As copy_to_lds, with a full 64-bit source address per lane (gathers from a block pool).
+__device__ __forceinline__ void copy_to_lds_addr(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+// A wavefront-uniform pointer the compiler cannot prove uniform, moved to SGPRs (the
+// scalar base of copy_to_lds must be in SGPRs).
+__device__ __forceinline__ const char* uniform_ptr(const char* ptr) {
+  const uint64_t a = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Wait until at most N vector-memory operations of this wavefront are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -182,10 +207,13 @@ constexpr int min_waves_per_eu() { return 2 * 2 * kBN * D * (int)sizeof(T) <= 80
 // SPLIT: the split-KV form (no mask): workgroup (split, head, query block) covers the
 // keys [split * chunk, min(Nk, (split + 1) * chunk)) and writes its O (normalised by its
 // own l) and logsumexp to the float32 partial buffers; mha_merge_kernel combines them.
-template <typename T, int D, bool CAUSAL, bool SPLIT = false>
+// PAGED (with SPLIT): K and V are gathered from block pools [num_blocks][H][bs][d]
+// through the block table; head b*H + h uses keys [0, seq_lens[b]).
+template <typename T, int D, bool CAUSAL, bool SPLIT = false, bool PAGED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<T, D>())))
 void mha_fwd_kernel(Params p) {
   static_assert(!(SPLIT && CAUSAL), "the split-KV form has no mask");
+  static_assert(!PAGED || SPLIT, "paged K/V uses the split-KV form");
   constexpr bool k16 = sizeof(T) == 2;         // bf16 or fp16 inputs
   typedef typename Half16<T>::v8 h8_t;
   constexpr int RB = D * (int)sizeof(T);        // bytes per K/V row
@@ -216,7 +244,13 @@ void mha_fwd_kernel(Params p) {
   int qb = id - bh * p.nqb;
   if (CAUSAL) qb = p.nqb - 1 - qb;
   const int N = p.N;                            // query rows
-  const int Nk = SPLIT ? p.Nk : N;              // keys
+  int seq_b = 0, head_h = 0;                    // paged: sequence and head of this workgroup
+  int Nk = SPLIT ? p.Nk : N;                    // keys
+  if constexpr (PAGED) {
+    seq_b = bh / p.H;
+    head_h = bh - seq_b * p.H;
+    Nk = min(max(p.seq_lens[seq_b], 0), p.max_blocks << p.bs_log2);
+  }
   const int kbeg = SPLIT ? split * p.chunk : 0; // this workgroup's keys: [kbeg, kend)
   const int kend = SPLIT ? min(Nk, kbeg + p.chunk) : N;
   const int q0 = qb * kBM;
@@ -229,7 +263,10 @@ void mha_fwd_kernel(Params p) {
   const char* Vbase = (const char*)((const T*)p.v + khead);
 
   const int kv_end = CAUSAL ? min(N, q0 + kBM) : kend;
-  const int ntiles = (kv_end - kbeg + kBN - 1) / kBN;
+  const int ntiles = PAGED ? max(0, (kv_end - kbeg + kBN - 1) / kBN) : (kv_end - kbeg + kBN - 1) / kBN;
+  // paged: a key range that starts past this sequence's end has nothing to do; the merge
+  // reads only the ranges below the sequence's key count
+  if (PAGED && ntiles == 0) return;
 
   // --- tile loader: thread (wave, lane) copies kLoads 16-byte chunks of K and of V.
   // Load j of a thread fills LDS bytes [(j*kWaves + wave)*1024, +1024); the swizzle is
@@ -248,12 +285,56 @@ void mha_fwd_kernel(Params p) {
   }
   const int ld_row0 = ld_row[0];
   const unsigned ld_off0 = (unsigned)(ld_row0 * RB + ld_chunk[0] * 16);
+
+  // --- paged K/V: key j of this sequence is row j % bs of block table[j / bs], and a
+  // block holds, per head, bs contiguous rows.  The table entries of a tile are read one
+  // step before its copies are issued, into ent[], with plain loads that the vmcnt(0)
+  // wait opening every step covers.  With bs >= kBN a tile (kBN-aligned) lies inside one
+  // block: one entry, a uniform base and the usual offsets.  Smaller blocks take one
+  // entry and a 64-bit address per copied row.  Entries are clamped into the pool, so a
+  // bad table gives wrong values, never an access outside the pools.
+  int ent[kLoads];
+  const int* btab = nullptr;
+  int bsl = 0;
+  if constexpr (PAGED) btab = p.block_table + (size_t)seq_b * p.max_blocks;
+  if constexpr (PAGED) bsl = p.bs_log2;
+  const bool big_blocks = bsl >= 6;
+  auto fetch_entries = [&](int t) __attribute__((always_inline)) {
+    const int k0 = kbeg + t * kBN;
+    if (big_blocks) {
+      ent[0] = btab[min(k0 + ld_row0, kend - 1) >> bsl];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) ent[j] = btab[min(k0 + ld_row[j], kend - 1) >> bsl];
+    }
+  };
+  // byte offset in a pool of row `key` (of this sequence and head) stored in block blk
+  auto pool_offset = [&](int blk, int key) __attribute__((always_inline)) {
+    blk = min(max(blk, 0), p.num_blocks - 1);
+    return ((((size_t)blk * p.H + head_h) << bsl) + (size_t)(key & ((1 << bsl) - 1))) * RB;
+  };
+
   auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
     const int k0 = kbeg + t * kBN;
     const char* kg = Kbase + (size_t)k0 * RB;
     const char* vg = Vbase + (size_t)k0 * RB;
     char* lk = smem + buf * 2 * kTileBytes;
     char* lv = lk + kTileBytes;
+    if constexpr (PAGED) {
+      if (!big_blocks) {
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+          const size_t off = pool_offset(ent[j], min(k0 + ld_row[j], kend - 1)) + ld_chunk[j] * 16;
+          const int dst = (j * kWaves + wave) * 1024;
+          copy_to_lds_addr((const char*)p.k + off, lds_addr(lk + dst));
+          copy_to_lds_addr((const char*)p.v + off, lds_addr(lv + dst));
+        }
+        return;
+      }
+      const size_t base = pool_offset(__builtin_amdgcn_readfirstlane(ent[0]), k0);
+      kg = uniform_ptr((const char*)p.k + base);
+      vg = uniform_ptr((const char*)p.v + base);
+    }
     if (k0 + kBN <= kend) {
 #pragma unroll
       for (int j = 0; j < kLoads; ++j) {
@@ -467,6 +548,9 @@ void mha_fwd_kernel(Params p) {
     wait_vmcnt<0>();
     tile_barrier();
     if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+    if constexpr (PAGED) {
+      if (t + 2 < ntiles) fetch_entries(t + 2);
+    }
     const int k0 = kbeg + t * kBN;
     if (SPLIT && qw >= N) return;                      // no query row in this wavefront
     if (!CAUSAL || k0 <= qw + kQW - 1) {               // else: every key is after every row
@@ -474,7 +558,11 @@ void mha_fwd_kernel(Params p) {
       compute_tile(smem + buf * 2 * kTileBytes, smem + buf * 2 * kTileBytes + kTileBytes, k0, need_mask);
     }
   };
+  if constexpr (PAGED) fetch_entries(0);
   issue_tile(0, 0);
+  if constexpr (PAGED) {
+    if (ntiles > 1) fetch_entries(1);
+  }
   for (int t = 0; t < ntiles; t += 2) {
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
@@ -570,11 +658,24 @@ __global__ __launch_bounds__(kMergeThreads) void mha_merge_kernel(Params p) {
   const size_t row = blockIdx.x;                      // (b*H + h) * N + query row
   const size_t stride = (size_t)p.BH * (size_t)p.N;   // between splits
   const int t = threadIdx.x;
+  int splits = p.splits;
+  if (p.seq_lens != nullptr) {
+    // paged: only the key ranges below this sequence's key count were written
+    const int b = (int)(row / p.N) / p.H;
+    const int len = min(max(p.seq_lens[b], 0), p.max_blocks << p.bs_log2);
+    splits = (len + p.chunk - 1) / p.chunk;
+    if (splits == 0) {
+      // no keys: the empty sum gives O = 0 and lse = log 0 = -inf
+      for (int c = t; c < D; c += kMergeThreads) ((T*)p.o)[row * D + c] = (T)0.f;
+      if (t == 0) p.lse[row] = -__builtin_inff();
+      return;
+    }
+  }
   float m = -__builtin_inff();
-  for (int s = t; s < p.splits; s += kMergeThreads) m = fmaxf(m, p.part_lse[s * stride + row]);
+  for (int s = t; s < splits; s += kMergeThreads) m = fmaxf(m, p.part_lse[s * stride + row]);
   const float M = block_reduce(m, red, true);
   float sum = 0.f;
-  for (int s = t; s < p.splits; s += kMergeThreads) {
+  for (int s = t; s < splits; s += kMergeThreads) {
     const float e = __builtin_amdgcn_exp2f((p.part_lse[s * stride + row] - M) * kLog2e);
     sum += e;
     if (s < kMergeLdsWeights) wts[s] = e;
@@ -583,7 +684,7 @@ __global__ __launch_bounds__(kMergeThreads) void mha_merge_kernel(Params p) {
   const float invL = 1.0f / L;
   for (int c = t; c < D; c += kMergeThreads) {
     float o = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
+    for (int s = 0; s < splits; ++s) {
       const float w = s < kMergeLdsWeights ? wts[s]
                                            : __builtin_amdgcn_exp2f((p.part_lse[s * stride + row] - M) * kLog2e);
       o += w * p.part_o[(s * stride + row) * D + c];
@@ -593,9 +694,9 @@ __global__ __launch_bounds__(kMergeThreads) void mha_merge_kernel(Params p) {
   if (t == 0) p.lse[row] = M + __builtin_amdgcn_logf(L) * kLn2;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED = false>
 hipError_t launch_split(const Params& p, hipStream_t stream) {
-  hipLaunchKernelGGL((mha_fwd_kernel<T, D, false, true>), dim3(p.total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((mha_fwd_kernel<T, D, false, true, PAGED>), dim3(p.total), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((mha_merge_kernel<T, D>), dim3(p.BH * p.N), dim3(kMergeThreads), 0, stream, p);
@@ -654,6 +755,40 @@ hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void*
   if (dtype == 1) return d == 64 ? launch_split<__bf16, 64>(p, stream) : launch_split<__bf16, 128>(p, stream);
   if (dtype == 2) return d == 64 ? launch_split<_Float16, 64>(p, stream) : launch_split<_Float16, 128>(p, stream);
   return d == 64 ? launch_split<float, 64>(p, stream) : launch_split<float, 128>(p, stream);
+}
+
+hipError_t launch_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const int* block_table,
+                            const int* seq_lens, void* o, float* lse, int B, int H, int Nq, int d, float scale,
+                            int dtype, int num_blocks, int bs_log2, int max_blocks, int splits, int chunk,
+                            float* part_o, float* part_lse, hipStream_t stream) {
+  Params p;
+  p.q = q;
+  p.k = k_pool;
+  p.v = v_pool;
+  p.o = o;
+  p.lse = lse;
+  p.N = Nq;
+  p.nqb = (Nq + kBM - 1) / kBM;
+  p.Nk = max_blocks << bs_log2;
+  p.chunk = chunk;
+  p.splits = splits;
+  p.BH = B * H;
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  p.total = p.nqb * p.BH * splits;
+  p.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
+  p.scale2 = (scale != 0.f ? fabsf(scale) : 1.f) * kLog2e;
+  p.H = H;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.max_blocks = max_blocks;
+  p.num_blocks = num_blocks;
+  p.bs_log2 = bs_log2;
+  if (dtype == 1)
+    return d == 64 ? launch_split<__bf16, 64, true>(p, stream) : launch_split<__bf16, 128, true>(p, stream);
+  if (dtype == 2)
+    return d == 64 ? launch_split<_Float16, 64, true>(p, stream) : launch_split<_Float16, 128, true>(p, stream);
+  return d == 64 ? launch_split<float, 64, true>(p, stream) : launch_split<float, 128, true>(p, stream);
 }
 
 }  // namespace mha_impl

@@ -21,6 +21,15 @@ hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               int Nq, int Nk, int d, float scale, int dtype, int splits, int chunk,
                               float* part_o, float* part_lse, hipStream_t stream);
 
+// Enqueue the paged split-KV forward: as launch_fwd_splitkv, with K and V gathered from
+// block pools [num_blocks][H][2^bs_log2][d] through block_table [B][max_blocks]; sequence
+// b uses keys [0, seq_lens[b]) (clamped to [0, max_blocks << bs_log2]).  part_o /
+// part_lse are sized for `splits` ranges of `chunk` keys.  Arguments validated.
+hipError_t launch_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const int* block_table,
+                            const int* seq_lens, void* o, float* lse, int B, int H, int Nq, int d, float scale,
+                            int dtype, int num_blocks, int bs_log2, int max_blocks, int splits, int chunk,
+                            float* part_o, float* part_lse, hipStream_t stream);
+
 }  // namespace mha_impl
 
 #endif  // MHA_LAUNCH_H_

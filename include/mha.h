@@ -31,6 +31,7 @@
 #define MHA_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -155,6 +156,78 @@ size_t mha_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int s
  * float32 LSE (the float32 partials are extra, implementation traffic).  Host only.
  */
 double mha_fwd_splitkv_bytes(int B, int H, int Nq, int Nk, int d, mha_dtype dtype);
+
+/*
+ * Paged split-KV forward (decoding against a paged key/value cache).
+ *
+ * The paged attention of the ML-Triton paper, section 3.2 (Figures 8 and 9) and
+ * section 4.3: each sequence's keys and values sit in fixed-size blocks scattered over
+ * a pool and are reached through a block table; the attention is unchanged.  The
+ * pages fix no layout, so this library defines one:
+ *
+ *   k_pool, v_pool  [num_blocks, H, block_size, d] of `dtype` (device): a block holds
+ *                   block_size consecutive keys of every head, each head's rows
+ *                   contiguous;
+ *   block_table     [B, max_blocks] int32 (device): key j of sequence b is row
+ *                   j % block_size of physical block block_table[b][j / block_size];
+ *   seq_lens        [B] int32 (device): sequence b has keys 0 .. seq_lens[b]-1;
+ *   q, o            [B, H, Nq, d] of `dtype`;  lse  [B, H, Nq] float32 (device).
+ *
+ * Every query row of sequence b attends to all of its keys (no mask); O and lse are
+ * those of the definition above over the gathered keys, computed with the split-KV
+ * merge.  A sequence with no keys gives O = 0 and lse = -inf.  The table and the
+ * lengths are read on the device only: a length is clamped to [0, max_blocks *
+ * block_size] and a table entry into [0, num_blocks), so bad values give wrong
+ * numbers, never an access outside the pools; entries past a sequence's last block
+ * are never used.
+ *
+ *   block_size  a power of two, 16 .. 65536 (else MHA_ERR_UNSUPPORTED)
+ *   splits      key ranges per sequence over max_blocks * block_size keys; 0 =
+ *               automatic (mha_fwd_paged_splits).  A range past a sequence's end
+ *               costs one workgroup that exits at once.
+ *   workspace   as for mha_fwd_splitkv, of at least mha_fwd_paged_workspace_size(...)
+ *               bytes.
+ *   other arguments as for mha_fwd_splitkv.
+ *
+ * Errors as for mha_fwd_splitkv, with MHA_ERR_INVALID_ARG for a null table, lengths
+ * or pool, num_blocks or max_blocks < 1, and MHA_ERR_UNSUPPORTED for a table or
+ * lengths pointer not 4-byte aligned or max_blocks * block_size above 2^30.
+ */
+mha_status mha_fwd_paged(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                         int B, int H, int Nq, int d, int num_blocks, int block_size,
+                         int max_blocks, float scale, mha_dtype dtype, int splits,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mha_fwd_paged_splits -- the number of key ranges mha_fwd_paged will use for a request
+ * of `splits` (0: automatic, as mha_fwd_splitkv_splits with Nk = max_blocks *
+ * block_size).  0 for invalid sizes.  Host only.
+ */
+int mha_fwd_paged_splits(int B, int H, int Nq, int block_size, int max_blocks, int splits);
+
+/*
+ * mha_fwd_paged_workspace_size -- bytes of workspace mha_fwd_paged needs:
+ * resolved_splits * B * H * Nq * (d + 1) * 4.  0 for invalid sizes.  Host only.
+ */
+size_t mha_fwd_paged_workspace_size(int B, int H, int Nq, int d, int block_size, int max_blocks,
+                                    int splits);
+
+/* mha_fwd_paged_validate -- the argument checks of mha_fwd_paged alone, host only. */
+mha_status mha_fwd_paged_validate(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  const void* o, const float* lse, int B, int H, int Nq, int d,
+                                  int num_blocks, int block_size, int max_blocks, float scale,
+                                  mha_dtype dtype, int splits, const void* workspace,
+                                  size_t workspace_bytes);
+
+/*
+ * mha_fwd_paged_bytes -- algorithmic HBM traffic of one mha_fwd_paged call over
+ * total_keys keys in all (the sum of seq_lens): Q read and O written, the K and V rows
+ * of every key read once, plus the float32 LSE.  Table and length reads (4 bytes per
+ * block and per sequence) and the float32 partials are not counted.  Host only.
+ */
+double mha_fwd_paged_bytes(int B, int H, int Nq, long long total_keys, int d, mha_dtype dtype);
 
 /* mha_status_string -- static, human-readable text for a status code. */
 const char* mha_status_string(mha_status status);

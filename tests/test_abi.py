@@ -137,3 +137,56 @@ def test_splitkv_partition(B, H, Nq, Nk, splits):
     assert mha.mha_fwd_splitkv_workspace_size(B, H, Nq, Nk, 128, splits) == s * B * H * Nq * 129 * 4
     assert mha.mha_fwd_splitkv_bytes(B, H, Nq, Nk, 128, BF16) == \
         (2 * Nq + 2 * Nk) * B * H * 128 * 2 + 4 * B * H * Nq
+
+
+def pv(**kw):
+    a = dict(q=P, kp=P, vp=P, bt=P, sl=P, o=P, lse=P, B=4, H=8, Nq=1, d=128, nb=100, bs=16, mb=64,
+             scale=0.1, dtype=BF16, splits=0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return mha.mha_fwd_paged_validate(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["o"], a["lse"], a["B"],
+                                      a["H"], a["Nq"], a["d"], a["nb"], a["bs"], a["mb"], a["scale"],
+                                      a["dtype"], a["splits"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(dtype=F32, d=64, bs=256), OK), (dict(dtype=F16, splits=3, bs=65536, mb=16), OK),
+    (dict(bt=P + 4, sl=P + 12), OK), (dict(bs=32, Nq=7), OK),
+    (dict(bt=0), INVALID), (dict(sl=0), INVALID), (dict(kp=0), INVALID), (dict(ws=0), INVALID),
+    (dict(wsb=16), INVALID), (dict(nb=0), INVALID), (dict(mb=0), INVALID), (dict(Nq=0), INVALID),
+    (dict(splits=-1), INVALID), (dict(dtype=5), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(bs=8), UNSUPPORTED), (dict(bs=48), UNSUPPORTED), (dict(bs=131072), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED), (dict(bt=P + 2), UNSUPPORTED), (dict(sl=P + 1), UNSUPPORTED),
+    (dict(vp=P + 8), UNSUPPORTED), (dict(bs=65536, mb=1 << 15), UNSUPPORTED),
+])
+def test_paged_validate(kw, code):
+    assert pv(**kw) == code
+
+
+def test_paged_rejects_before_launch():
+    assert mha.mha_fwd_paged(P, P, P, P, P, P, P, 1, 1, 1, 64, 10, 16, 4, 0.1, BF16, 0, 0, 0, 0) == INVALID
+    assert mha.mha_fwd_paged(P, P, P, P, P, P, P, 1, 1, 1, 64, 10, 24, 4, 0.1, BF16, 0, P, 1 << 20, 0) \
+        == UNSUPPORTED
+
+
+@pytest.mark.parametrize("B,H,Nq,bs,mb", [(1, 1, 1, 16, 1), (64, 8, 1, 16, 512), (16, 32, 1, 64, 256),
+                                          (8, 8, 1, 256, 128), (32, 16, 4, 32, 128), (2, 2, 200, 128, 3)])
+@pytest.mark.parametrize("splits", [0, 1, 3, 10000])
+def test_paged_partition(B, H, Nq, bs, mb, splits):
+    max_keys = bs * mb
+    s = mha.mha_fwd_paged_splits(B, H, Nq, bs, mb, splits)
+    tiles = -(-max_keys // 64)
+    assert 1 <= s <= tiles
+    if splits > 0:
+        assert s <= splits
+    else:
+        # the split-KV choice over the longest possible sequence
+        assert s == mha.mha_fwd_splitkv_splits(B, H, Nq, max_keys, 0)
+    assert mha.mha_fwd_paged_workspace_size(B, H, Nq, 128, bs, mb, splits) == s * B * H * Nq * 129 * 4
+    assert mha.mha_fwd_paged_splits(B, H, Nq, 24, mb, splits) == 0
+    assert mha.mha_fwd_paged_workspace_size(B, H, Nq, 128, bs, 0, splits) == 0
+
+
+def test_paged_bytes():
+    assert mha.mha_fwd_paged_bytes(64, 8, 1, 263473, 128, BF16) == \
+        (2 * 64 + 2 * 263473) * 8 * 128 * 2 + 4 * 64 * 8
+    assert mha.mha_fwd_paged_bytes(2, 3, 4, 5, 64, F32) == (2 * 2 * 4 + 2 * 5) * 3 * 64 * 4 + 4 * 2 * 3 * 4

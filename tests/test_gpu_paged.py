@@ -1,0 +1,191 @@
+"""GPU parity of the paged split-KV forward (mha_fwd_paged): query rows against keys and
+values scattered over a block pool and reached through a block table.  Compared element
+by element (small shapes) or on sampled rows (the paged workloads) with the CPU
+oracle's paged definition; pool rows no sequence owns are filled with large values so
+that reading one shows.  Tolerances as for the fused kernel: fp32 1e-4 / 1e-4, bf16
+2e-2 / 1e-3, fp16 5e-3 / 1e-3 (max |dO|, max |dLSE|)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import head_attention_fa2_amd as mha
+import mha_inputs
+import oracle
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+_POISON = {"bf16": (0x4270, 0x4700), "f16": (0x5300, 0x7000), "f32": (60.0, 3.0e4)}  # K, V
+
+
+def _poison_unowned(kp, vp, table, lens, dtype):
+    """Fill pool rows that no sequence owns with large K (logit ~ 60*|q|) and V values."""
+    bs = kp.shape[2]
+    owned = np.zeros(kp.shape[:3], dtype=bool)
+    for b, L in enumerate(lens):
+        j = np.arange(int(L))
+        owned[table[b, j // bs], :, j % bs] = True
+    pk, pv = _POISON[dtype]
+    kp, vp = kp.copy(), vp.copy()
+    kp[~owned] = pk
+    vp[~owned] = pv
+    return kp, vp
+
+
+def _run(q, kp, vp, table, lens, dtype, scale, splits, workspace=None):
+    tq, tk, tv = (gu.to_device(x, dtype) for x in (q, kp, vp))
+    tt = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).cuda()
+    tl = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
+    o, lse = mha.fwd_paged(tq, tk, tv, tt, tl, scale=scale, splits=splits, workspace=workspace)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _oracle(q, kp, vp, table, lens, dtype, scale):
+    return oracle.paged_attention_forward(oracle.decode(q, dtype), oracle.decode(kp, dtype),
+                                          oracle.decode(vp, dtype), table, lens, scale=scale)
+
+
+def _check(o, lse, o_ref, l_ref, dtype, what):
+    tol_o, tol_l = gu.TOL[dtype]
+    empty = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(lse), empty), what
+    assert np.all(o[empty] == 0.0), what
+    full = ~empty
+    eo = float(np.max(np.abs(o[full] - o_ref[full]))) if full.any() else 0.0
+    el = float(np.max(np.abs(lse[full] - l_ref[full]))) if full.any() else 0.0
+    print(f"{what}: max|dO|={eo:.3e} max|dLSE|={el:.3e}, {int(empty.sum())} empty rows", flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse[full])), what
+    assert eo <= tol_o and el <= tol_l, what
+
+
+CASES = [
+    # (B, H, Nq, d, dtype, block_size, lens, splits)
+    (1, 1, 1, 64, "bf16", 16, [1], 0),
+    (3, 2, 1, 128, "bf16", 16, [15, 16, 17], 0),
+    (4, 2, 1, 128, "bf16", 16, [0, 63, 64, 65], 2),
+    (2, 3, 2, 64, "f16", 32, [1000, 33], 3),
+    (3, 2, 4, 128, "bf16", 64, [64, 700, 129], 0),
+    (2, 2, 1, 128, "bf16", 128, [4097, 1], 5),
+    (2, 1, 3, 64, "f32", 256, [300, 513], 2),
+    (2, 2, 33, 128, "f32", 16, [200, 95], 0),
+    (5, 2, 1, 64, "bf16", 32, [0, 0, 2000, 5, 1024], 0),
+    (2, 2, 130, 64, "bf16", 64, [1500, 64], 4),
+    (1, 4, 1, 128, "f16", 16, [5000], 1000),
+    (2, 2, 1, 128, "bf16", 1024, [3000, 2048], 0),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,d,dtype,bs,lens,splits", CASES)
+def test_paged_elementwise(B, H, Nq, d, dtype, bs, lens, splits):
+    seed = 700 + B * 31 + Nq + d + bs + sum(lens)
+    q, kp, vp, table, sl = mha_inputs.draw_paged(B, H, Nq, d, dtype, bs, lens, seed, spare=3)
+    kp, vp = _poison_unowned(kp, vp, table, sl, dtype)
+    scale = 1 / math.sqrt(d)
+    o, lse = _run(q, kp, vp, table, sl, dtype, scale, splits)
+    o_ref, l_ref = _oracle(q, kp, vp, table, sl, dtype, scale)
+    _check(o, lse, o_ref, l_ref, dtype, f"paged B{B} H{H} Nq{Nq} d{d} {dtype} bs{bs} lens={lens} splits={splits}")
+
+
+@pytest.mark.parametrize("bs", [16, 64, 256])
+def test_paged_identity_layout_equals_splitkv(bs):
+    # Sequence b's blocks are consecutive and in order: the pool is the contiguous cache,
+    # and with the same key ranges the paged path must reproduce the split-KV result.
+    B, H, Nq, d, n = 2, 3, 2, 128, 2048
+    q, k, v = mha_inputs.draw((B, H, Nq, d), "bf16", 51 + bs, kv_shape=(B, H, n, d))
+    mb = n // bs
+    kp = k.reshape(B, H, mb, bs, d).transpose(0, 2, 1, 3, 4).reshape(B * mb, H, bs, d)
+    vp = v.reshape(B, H, mb, bs, d).transpose(0, 2, 1, 3, 4).reshape(B * mb, H, bs, d)
+    table = np.arange(B * mb, dtype=np.int32).reshape(B, mb)
+    o1, l1 = _run(q, kp, vp, table, np.array([n, n]), "bf16", 0.1, 4)
+    tq, tk, tv = (gu.to_device(x, "bf16") for x in (q, k, v))
+    o2, l2 = mha.fwd_splitkv(tq, tk, tv, scale=0.1, splits=4)
+    torch.cuda.synchronize()
+    o2 = o2.float().cpu().numpy().astype(np.float64)
+    l2 = l2.cpu().numpy().astype(np.float64)
+    print(f"bs{bs}: paged == split-KV bit for bit: {np.array_equal(o1, o2) and np.array_equal(l1, l2)}", flush=True)
+    assert float(np.max(np.abs(o1 - o2))) <= 2e-2 and float(np.max(np.abs(l1 - l2))) <= 1e-3
+
+
+def test_paged_large_logits_and_scales():
+    lens = [900, 77]
+    for sigma, scale in ((5.0, 0.5), (1.0, -0.3), (1.0, 0.0)):
+        q, kp, vp, table, sl = mha_inputs.draw_paged(2, 2, 3, 64, "bf16", 16, lens, int(sigma * 10) + 9, spare=2,
+                                                     dist=mha_inputs.Dist("normal", sigma))
+        o, lse = _run(q, kp, vp, table, sl, "bf16", scale, 3)
+        o_ref, l_ref = _oracle(q, kp, vp, table, sl, "bf16", scale)
+        _check(o, lse, o_ref, l_ref, "bf16", f"paged sigma={sigma} scale={scale}")
+
+
+def test_paged_clamps_bad_lengths_and_entries():
+    # Lengths beyond the table and entries outside the pool are clamped on the device:
+    # the result is that of the clamped inputs.
+    bs, lens = 16, [40, 20]
+    q, kp, vp, table, sl = mha_inputs.draw_paged(2, 2, 1, 64, "bf16", bs, lens, 77, spare=2)
+    nb, mb = kp.shape[0], table.shape[1]
+    bad_table = table.copy()
+    bad_table[0, 1] = nb + 5
+    bad_table[1, 0] = -3
+    bad_lens = np.array([1 << 20, 20], dtype=np.int32)
+    o, lse = _run(q, kp, vp, bad_table, bad_lens, "bf16", 0.125, 0)
+    clamped_lens = np.minimum(bad_lens, mb * bs)
+    clamped_table = np.clip(bad_table, 0, nb - 1)
+    o_ref, l_ref = _oracle(q, kp, vp, clamped_table, clamped_lens, "bf16", 0.125)
+    _check(o, lse, o_ref, l_ref, "bf16", "clamped table and lengths")
+
+
+def test_paged_workspace_reused_by_consecutive_calls():
+    ws = torch.empty(mha.mha_fwd_paged_workspace_size(3, 4, 2, 128, 16, 256, 6), dtype=torch.uint8, device="cuda")
+    for (B, H, Nq, lens, splits) in ((3, 4, 2, [4000, 100, 2500], 6), (2, 2, 1, [700, 3], 3)):
+        q, kp, vp, table, sl = mha_inputs.draw_paged(B, H, Nq, 128, "bf16", 16, lens, sum(lens))
+        o, lse = _run(q, kp, vp, table, sl, "bf16", 0.09, splits, workspace=ws)
+        o_ref, l_ref = _oracle(q, kp, vp, table, sl, "bf16", 0.09)
+        _check(o, lse, o_ref, l_ref, "bf16", f"shared workspace lens={lens}")
+
+
+@pytest.mark.parametrize("name", list(mha_inputs.PAGED))
+def test_paged_workload_sampled(name):
+    w = mha_inputs.PAGED[name]
+    q, kp, vp, table, sl = mha_inputs.draw_paged_workload(w)
+    tq, tk, tv = (gu.to_device(x, w.dtype) for x in (q, kp, vp))
+    tt, tl = torch.from_numpy(table).cuda(), torch.from_numpy(sl).cuda()
+    o, lse = mha.fwd_paged(tq, tk, tv, tt, tl, scale=w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rng = np.random.default_rng(w.seed)
+    seqs = sorted({int(rng.integers(w.B)) for _ in range(6)} | {0, w.B - 1})
+    picks = [(b, int(rng.integers(w.H)), int(rng.integers(w.Nq))) for b in seqs]
+    o_ref = np.empty((len(picks), w.d))
+    l_ref = np.empty(len(picks))
+    for n, (b, h, i) in enumerate(picks):
+        # only this sequence's blocks, renumbered 0..c-1 (renumbering changes nothing)
+        c = -(-int(sl[b]) // w.block_size)
+        used = table[b, :c]
+        ob, lb = oracle.paged_attention_forward(
+            oracle.decode(q[b:b + 1, h:h + 1, i:i + 1], w.dtype), oracle.decode(kp[used, h:h + 1], w.dtype),
+            oracle.decode(vp[used, h:h + 1], w.dtype), np.arange(c)[None], sl[b:b + 1], scale=w.scale)
+        o_ref[n], l_ref[n] = ob[0, 0, 0], lb[0, 0, 0]
+    idx = torch.tensor(picks, dtype=torch.long, device=o.device)
+    og = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
+    lg = lse[idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy().astype(np.float64)
+    splits = mha.mha_fwd_paged_splits(w.B, w.H, w.Nq, w.block_size, table.shape[1], 0)
+    _check(og, lg, o_ref, l_ref, w.dtype, f"{name}, {len(picks)} sampled rows, {splits} splits")
+
+
+def test_paged_errors_raise():
+    q = torch.zeros(1, 1, 1, 64, device="cuda", dtype=torch.bfloat16)
+    kp = torch.zeros(4, 1, 16, 64, device="cuda", dtype=torch.bfloat16)
+    table = torch.zeros(1, 4, dtype=torch.int32, device="cuda")
+    lens = torch.ones(1, dtype=torch.int32, device="cuda")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mha.MhaError) as e:
+        mha.fwd_paged(q, kp, kp, table, lens, workspace=small)
+    assert e.value.status == mha.MHA_ERR_INVALID_ARG
+    kp24 = torch.zeros(4, 1, 24, 64, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(mha.MhaError) as e:
+        mha.fwd_paged(q, kp24, kp24, table, lens)
+    assert e.value.status == mha.MHA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        mha.fwd_paged(q, kp, kp, table.long(), lens)
