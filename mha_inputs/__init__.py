@@ -29,6 +29,9 @@ __all__ = [
     "DECODE",
     "PagedWorkload",
     "PAGED",
+    "GemmWorkload",
+    "GEMM",
+    "draw_gemm",
     "f32_to_bf16_bits",
     "f32_to_f16_bits",
     "draw",
@@ -191,6 +194,33 @@ PAGED: Dict[str, PagedWorkload] = {
 }
 
 
+@dataclass(frozen=True)
+class GemmWorkload:
+    """C [M, N] = A [M, K] @ B [K, N], row-major, N(0,1) operands."""
+
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype: str
+    seed: int
+
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+
+# Dense GEMM (the tiled contraction of the ML-Triton paper, sections 2 and 4.1).  The
+# pages keep only "m = 1k..16k, shapes from Llama-2 / Llama-3 layers": the token count
+# M runs over 1k..16k against three Llama-3-8B linear layers (hidden 4096, MLP 14336):
+# the attention output projection (K = N = 4096), the MLP up projection (K = 4096,
+# N = 14336) and the MLP down projection (K = 14336, N = 4096).
+GEMM: Dict[str, GemmWorkload] = {}
+for _i, ((_k, _n), _m) in enumerate(((kn, m) for kn in ((4096, 4096), (4096, 14336), (14336, 4096))
+                                     for m in (1024, 2048, 4096, 8192, 16384))):
+    _g = GemmWorkload(f"bf16_gemm_M{_m}_N{_n}_K{_k}", _m, _n, _k, "bf16", seed=400 + _i)
+    GEMM[_g.name] = _g
+
+
 def _sample(rng: np.random.Generator, shape, dist: Dist) -> np.ndarray:
     if dist.kind == "normal":
         x = rng.standard_normal(size=shape, dtype=np.float32)
@@ -273,3 +303,19 @@ def paged_lengths(w: PagedWorkload) -> np.ndarray:
 def draw_paged_workload(w: PagedWorkload):
     """Inputs of a named paged workload (see :func:`draw_paged`)."""
     return draw_paged(w.B, w.H, w.Nq, w.d, w.dtype, w.block_size, paged_lengths(w), w.seed + 1, w.spare)
+
+
+def draw_gemm(M: int, N: int, K: int, dtype: str, seed: int, dist: Dist = Dist("normal", 1.0)):
+    """A ``[M, K]`` and B ``[K, N]`` from ``seed`` (two child streams), encoded as for
+    :func:`draw`."""
+    if dtype not in ("f32", "bf16", "f16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    out = []
+    for child, shp in zip(np.random.SeedSequence(seed).spawn(2), ((M, K), (K, N))):
+        x = _sample(np.random.Generator(np.random.PCG64(child)), shp, dist)
+        if dtype == "bf16":
+            x = f32_to_bf16_bits(x)
+        elif dtype == "f16":
+            x = f32_to_f16_bits(x)
+        out.append(np.ascontiguousarray(x))
+    return out[0], out[1]

@@ -12,7 +12,9 @@ Contents:
     step as the FlashAttention-2 algorithm states it, used to check readings of the
     algorithm (deferred normalisation, masked tiles) on the CPU;
   * :mod:`oracle.paged` -- attention over a paged key/value cache (keys reached
-    through a block table), the plain definition applied to the gathered keys.
+    through a block table), the plain definition applied to the gathered keys;
+  * :mod:`oracle.matmul` -- the dense matrix product and the error bound of a float32
+    accumulated, once-rounded result.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against brute force in
 40-digit decimal arithmetic, a library attention routine in float64, closed forms
@@ -25,3 +27,4 @@ from .attention import (  # noqa: F401
 )
 from .online import attention_forward_tiled  # noqa: F401
 from .paged import gather_keys, paged_attention_forward  # noqa: F401
+from .matmul import gemm, gemm_error_bound  # noqa: F401

@@ -100,3 +100,15 @@ def test_paged_workloads():
         assert lens.shape == (w.B,) and lens.min() >= w.len_lo and lens.max() <= w.len_hi, name
         assert w.block_size & (w.block_size - 1) == 0 and w.block_size >= 16, name
         assert name.startswith(w.dtype) and f"_bs{w.block_size}_" in name, name
+
+
+def test_draw_gemm_and_workloads():
+    a, b = mi.draw_gemm(5, 7, 9, "bf16", seed=3)
+    assert a.shape == (5, 9) and b.shape == (9, 7) and a.dtype == np.uint16
+    a2, b2 = mi.draw_gemm(5, 7, 9, "bf16", seed=3)
+    np.testing.assert_array_equal(a, a2)
+    np.testing.assert_array_equal(b, b2)
+    assert not np.array_equal(mi.draw_gemm(5, 7, 9, "bf16", seed=4)[0], a)
+    assert len(mi.GEMM) == 15
+    for name, w in mi.GEMM.items():
+        assert name == f"bf16_gemm_M{w.M}_N{w.N}_K{w.K}" and w.flops() == 2.0 * w.M * w.N * w.K
