@@ -150,6 +150,54 @@ def time_gpu_paged(w, steps, warmup, dev, splits=0):
     return dict(total_ms=ev[0].elapsed_time(ev[1]), inputs=(q, kp, vp, table, lens), out=(o, lse))
 
 
+def time_gemm(w, steps, warmup, dev, torch_too=True):
+    """Time mha.gemm (and torch.matmul, the vendor library, for context) on a GEMM workload."""
+    import torch
+
+    import head_attention_fa2_amd as mha
+    import mha_inputs
+
+    a, b = mha_inputs.draw_gemm(w.M, w.N, w.K, w.dtype, w.seed)
+    ta, tb = _to_device(a, w.dtype, dev), _to_device(b, w.dtype, dev)
+    c = torch.empty((w.M, w.N), dtype=ta.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize(dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize(dev)
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    ms = timed(lambda: mha.gemm(ta, tb, out=c, stream=stream))
+    ms_torch = timed(lambda: torch.matmul(ta, tb, out=c)) if torch_too else None
+    mha.gemm(ta, tb, out=c, stream=stream)
+    torch.cuda.synchronize(dev)
+    return dict(ms=ms, ms_torch=ms_torch, inputs=(a, b), out=c)
+
+
+def parity_sample_gemm(w, inputs, out, n=8):
+    """Largest error / bound over sampled entries of C (<= 1 passes)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    a_bits, b_bits = inputs
+    rng = np.random.default_rng(w.seed + 1)
+    rows, cols = rng.integers(0, w.M, n), rng.integers(0, w.N, n)
+    cg = out[torch.from_numpy(rows).to(out.device)][:, torch.from_numpy(cols).to(out.device)]
+    cg = cg.float().cpu().numpy().astype(np.float64)
+    a, b = oracle.decode(a_bits[rows], w.dtype), oracle.decode(b_bits[:, cols], w.dtype)
+    ratio = np.abs(cg - oracle.gemm(a, b)) / oracle.gemm_error_bound(a, b, w.dtype)
+    return {"max_err_over_bound": float(ratio.max()), "entries": int(ratio.size)}
+
+
 def parity_sample_paged(w, inputs, out, n=6):
     """Max abs error of sampled output rows of a paged workload against the CPU oracle."""
     import numpy as np
@@ -238,6 +286,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time every workload (lines on stderr)")
     ap.add_argument("--decode", action="store_true",
                     help="also time the split-KV decode workloads (lines on stderr)")
+    ap.add_argument("--gemm", action="store_true",
+                    help="also time the dense GEMM workloads, with torch.matmul beside them (lines on stderr)")
     ap.add_argument("--paged", action="store_true",
                     help="also time the paged split-KV decode workloads (lines on stderr)")
     ap.add_argument("--pages-sweep", action="store_true",
@@ -328,6 +378,17 @@ def main():
                               "pct_of_hbm": round(100 * nbytes / (m * 1e-3) / 1e9 / HBM_GBS, 2),
                               "TFLOP/s": round(ww.credited_flops() / (m * 1e-3) / 1e12, 2),
                               "parity": parity_sample(ww, rr["inputs"], rr["out"], n=8)}),
+                  file=sys.stderr, flush=True)
+            del rr
+    if args.gemm:
+        for name, ww in mha_inputs.GEMM.items():
+            rr = time_gemm(ww, max(10, args.steps // 4), 5, dev)
+            tf = ww.flops() / (rr["ms"] * 1e-3) / 1e12
+            tft = ww.flops() / (rr["ms_torch"] * 1e-3) / 1e12
+            print(json.dumps({"workload": name, "M": ww.M, "N": ww.N, "K": ww.K, "ms": round(rr["ms"], 5),
+                              "TFLOP/s": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_TFLOPS[ww.dtype], 2),
+                              "torch_matmul_TFLOP/s": round(tft, 1), "vs_torch": round(tf / tft, 3),
+                              "parity": parity_sample_gemm(ww, rr["inputs"], rr["out"])}),
                   file=sys.stderr, flush=True)
             del rr
     if args.paged:

@@ -6,9 +6,10 @@ the C ABI of ``include/mha.h``).  This module only marshals arguments: the funct
 ``mha_fwd_splitkv``, ``mha_fwd_splitkv_validate``, ``mha_fwd_splitkv_splits``,
 ``mha_fwd_splitkv_workspace_size``, ``mha_fwd_splitkv_bytes``, ``mha_fwd_paged``,
 ``mha_fwd_paged_validate``, ``mha_fwd_paged_splits``, ``mha_fwd_paged_workspace_size``,
-``mha_fwd_paged_bytes``, ``mha_status_string`` and ``mha_version`` mirror the C entry
-points one to one, and :func:`fwd` / :func:`fwd_splitkv` / :func:`fwd_paged` are the
-PyTorch-facing conveniences (device memory and the stream
+``mha_fwd_paged_bytes``, ``mha_gemm``, ``mha_gemm_validate``, ``mha_gemm_flops``,
+``mha_gemm_bytes``, ``mha_status_string`` and ``mha_version`` mirror the C entry points
+one to one, and :func:`fwd` / :func:`fwd_splitkv` / :func:`fwd_paged` / :func:`gemm` are
+the PyTorch-facing conveniences (device memory and the stream
 come from torch; nothing is computed in Python).  There is no fallback: if the library is not
 built or a call fails, an exception is raised.
 """
@@ -25,7 +26,8 @@ __all__ = [
     "mha_fwd_bytes", "mha_fwd_splitkv", "mha_fwd_splitkv_validate", "mha_fwd_splitkv_splits",
     "mha_fwd_splitkv_workspace_size", "mha_fwd_splitkv_bytes", "mha_fwd_paged", "mha_fwd_paged_validate",
     "mha_fwd_paged_splits", "mha_fwd_paged_workspace_size", "mha_fwd_paged_bytes", "mha_status_string",
-    "mha_version", "fwd", "fwd_splitkv", "fwd_paged", "MhaError",
+    "mha_version", "mha_gemm", "mha_gemm_validate", "mha_gemm_flops", "mha_gemm_bytes",
+    "fwd", "fwd_splitkv", "fwd_paged", "gemm", "MhaError",
 ]
 
 MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_HIP = 0, 1, 2, 3
@@ -86,6 +88,14 @@ def load() -> ctypes.CDLL:
     lib.mha_fwd_paged_workspace_size.restype = sz
     lib.mha_fwd_paged_bytes.argtypes = [i, i, i, ctypes.c_longlong, i, i]
     lib.mha_fwd_paged_bytes.restype = ctypes.c_double
+    lib.mha_gemm.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    lib.mha_gemm.restype = i
+    lib.mha_gemm_validate.argtypes = [vp, vp, vp, i, i, i, i]
+    lib.mha_gemm_validate.restype = i
+    lib.mha_gemm_flops.argtypes = [i, i, i]
+    lib.mha_gemm_flops.restype = ctypes.c_double
+    lib.mha_gemm_bytes.argtypes = [i, i, i, i]
+    lib.mha_gemm_bytes.restype = ctypes.c_double
     lib.mha_status_string.argtypes = [i]
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_version.argtypes = []
@@ -171,6 +181,23 @@ def mha_fwd_paged_workspace_size(B: int, H: int, Nq: int, d: int, block_size: in
 
 def mha_fwd_paged_bytes(B: int, H: int, Nq: int, total_keys: int, d: int, dtype: int) -> float:
     return load().mha_fwd_paged_bytes(B, H, Nq, total_keys, d, dtype)
+
+
+def mha_gemm(a: int, b: int, c: int, M: int, N: int, K: int, dtype: int, stream: int) -> int:
+    """Enqueue C = A.B on ``stream``."""
+    return load().mha_gemm(a, b, c, M, N, K, dtype, stream)
+
+
+def mha_gemm_validate(a: int, b: int, c: int, M: int, N: int, K: int, dtype: int) -> int:
+    return load().mha_gemm_validate(a, b, c, M, N, K, dtype)
+
+
+def mha_gemm_flops(M: int, N: int, K: int) -> float:
+    return load().mha_gemm_flops(M, N, K)
+
+
+def mha_gemm_bytes(M: int, N: int, K: int, dtype: int) -> float:
+    return load().mha_gemm_bytes(M, N, K, dtype)
 
 
 def mha_status_string(status: int) -> str:
@@ -330,3 +357,34 @@ def fwd_paged(q, k_pool, v_pool, block_table, seq_lens, scale: Optional[float] =
     if st != MHA_OK:
         raise MhaError(st)
     return out, lse
+
+
+def gemm(a, b, out=None, stream=None):
+    """``C = gemm(a, b)``: ``a [M, K] @ b [K, N]`` for contiguous bfloat16 or float16 CUDA
+    tensors of one dtype (float32 accumulation, C in the input dtype).  ``out`` may be
+    given to reuse a buffer.  Enqueued on ``stream`` (default: torch's current stream);
+    no sync.
+    """
+    import torch
+
+    _DTYPES = {torch.bfloat16: MHA_DTYPE_BF16, torch.float16: MHA_DTYPE_F16}
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("need a [M, K] and b [K, N]")
+    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
+        raise ValueError("a and b must be on the same GPU")
+    if a.dtype not in _DTYPES or b.dtype != a.dtype:
+        raise ValueError("a and b must both be bfloat16 or both float16")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous")
+    M, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    elif out.shape != (M, N) or out.dtype != a.dtype or out.device != a.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] tensor like a")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    st = mha_gemm(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, _DTYPES[a.dtype], stream.cuda_stream)
+    if st != MHA_OK:
+        raise MhaError(st)
+    return out

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmha.so")
 
-SOURCES = ["mha_fwd_kernel.hip", "mha_api.cpp"]
+SOURCES = ["mha_fwd_kernel.hip", "gemm_kernel.hip", "mha_api.cpp"]
 
 # -Xclang -target-feature -Xclang -packed-fp32-ops: never emit v_pk_{add,mul,fma}_f32.
 HIPCC_FLAGS = [

@@ -1,0 +1,261 @@
+// Dense GEMM for gfx950 (AMD Instinct MI355X, CDNA4): C = A.B with A [M, K] and
+// B [K, N] row-major in bf16 or fp16, float32 accumulation, C [M, N] rounded to the
+// input type (round to nearest even).
+//
+// This is the tiled contraction of "ML-Triton, A Multi-Level Compilation and Language
+// Extension to Triton GPU Programming", section 2 (a workgroup owns a block of C and
+// accumulates it over k-steps, then stores it once; section 4.1 measures it on
+// compute-bound LLM shapes), laid out for CDNA4:
+//  * A workgroup of 8 wavefronts owns a 256 x 256 block of C; the wavefronts form a
+//    2 x 4 grid and each accumulates a 128 x 64 sub-block in 8 float32 accumulators of
+//    v_mfma_f32_32x32x16_{bf16,f16} (128 VGPRs).  One workgroup per CU (128 KiB of LDS).
+//  * The product is formed transposed per 32 x 32 block, C^T = B^T.A^T, so that after
+//    the MFMA every lane holds 8 consecutive columns of one row of C (16-byte stores).
+//    The B^T operand comes from row-major B in LDS through ds_read_b64_tr_b16, the
+//    A^T operand from row-major A through ds_read_b128; the rows of B^T enter in an
+//    order that swaps bits 2 and 3 of the row index, which is what puts 8 consecutive
+//    columns in one lane.
+//  * k-steps of 64: the A (256 x 64) and B (64 x 256) tiles are copied HBM -> LDS with
+//    global_load_lds_dwordx4, double buffered with one barrier per k-step (the copy of
+//    step t+1 is in flight while step t is consumed).  LDS rows are XOR-swizzled in
+//    16-byte chunks so that both operand reads are free of bank conflicts.
+//  * Workgroup ids are renumbered so that each XCD gets a contiguous range of tiles,
+//    traversed in groups of 8 block-rows (the grouped order of the Triton tutorial's
+//    GEMM), so the workgroups resident on one XCD share A and B panels in its L2.
+//  * Ragged M and N: out-of-range rows / columns of A and B are read clamped and never
+//    stored.  Ragged K (a multiple of 8): the A chunks past K are zeroed in LDS once
+//    their copy has landed, so they add nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gfx950_lds.h"
+#include "mha_launch.h"
+#include "mha_layout.h"
+
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace mha_impl {
+namespace {
+
+using gfx950::copy_to_lds;
+using gfx950::lds_addr;
+using gfx950::tile_barrier;
+using gfx950::wait_vmcnt;
+using mha_layout::lds_inv;
+using mha_layout::lds_off;
+using mha_layout::v_operand_off;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+template <typename T>
+struct Mfma;
+template <>
+struct Mfma<__bf16> {
+  typedef bf16x8_t v8;
+  static __device__ __forceinline__ f32x16_t mma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<_Float16> {
+  typedef f16x8_t v8;
+  static __device__ __forceinline__ f32x16_t mma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+constexpr int kBM = 256;                   // rows of C per workgroup
+constexpr int kBN = 256;                   // columns of C per workgroup
+constexpr int kBK = 64;                    // k per step
+constexpr int kWavesM = 2, kWavesN = 4;
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMB = kBM / kWavesM / 32;    // 32-row blocks per wavefront (4)
+constexpr int kNB = kBN / kWavesN / 32;    // 32-column blocks per wavefront (2)
+constexpr int kATile = kBM * kBK * 2;      // bytes of the A tile (rows of 8 chunks)
+constexpr int kBTile = kBK * kBN * 2;      // bytes of the B tile (rows of 32 chunks)
+constexpr int kStage = kATile + kBTile;
+constexpr int kLoadsA = kATile / 16 / kThreads;
+constexpr int kLoadsB = kBTile / 16 / kThreads;
+constexpr int kGroupM = 8;                 // block-rows per group of the tile order
+static_assert(kLoadsA * 16 * kThreads == kATile && kLoadsB * 16 * kThreads == kBTile, "even split");
+
+struct GemmParams {
+  const void* a;
+  const void* b;
+  void* c;
+  int M, N, K;
+  int tiles_m, tiles_n, total;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
+  typedef typename Mfma<T>::v8 v8_t;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];   // [buf][A, B]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_m = wave / kWavesN, wave_n = wave % kWavesN;
+  const int G = lane >> 5;
+
+  // --- workgroup -> tile: contiguous id ranges per XCD, grouped block-row order.
+  int id = blockIdx.x;
+  if ((p.total & 7) == 0) id = (id & 7) * (p.total >> 3) + (id >> 3);
+  const int group = kGroupM * p.tiles_n;
+  const int first_m = id / group * kGroupM;
+  const int gsize = min(p.tiles_m - first_m, kGroupM);
+  const int in_group = id % group;
+  const int m0 = (first_m + in_group % gsize) * kBM;
+  const int n0 = in_group / gsize * kBN;
+  const int M = p.M, N = p.N, K = p.K;
+  const unsigned lda = (unsigned)K * 2u, ldb = (unsigned)N * 2u;
+
+  // --- tile loader.  Load j of a thread fills LDS slot (j*kWaves + wave)*64 + lane of
+  // its tile; lds_inv gives the (row, chunk) that slot holds.  Byte offsets are 32-bit
+  // (the host checks that A and B are under 4 GiB).
+  unsigned a_row[kLoadsA];   // byte offset of the (clamped) A row
+  int a_k[kLoadsA];          // k of the chunk within a tile
+  int b_row[kLoadsB];        // k row within a tile
+  unsigned b_col[kLoadsB];   // byte offset of the (clamped) column chunk
+#pragma unroll
+  for (int j = 0; j < kLoadsA; ++j) {
+    int r, c;
+    lds_inv<8>((j * kWaves + wave) * 64 + lane, r, c);
+    a_row[j] = (unsigned)min(m0 + r, M - 1) * lda;
+    a_k[j] = c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < kLoadsB; ++j) {
+    int r, c;
+    lds_inv<32>((j * kWaves + wave) * 64 + lane, r, c);
+    b_row[j] = r;
+    b_col[j] = (unsigned)min(n0 / 8 + c, N / 8 - 1) * 16u;
+  }
+  const int nk = (K + kBK - 1) / kBK;
+
+  auto issue = [&](int t, int buf) __attribute__((always_inline)) {
+    const int k0 = t * kBK;
+    char* sa = smem + buf * kStage;
+    char* sb = sa + kATile;
+#pragma unroll
+    for (int j = 0; j < kLoadsA; ++j) {
+      // chunks past K read the last chunk of the row; zeroed after they land
+      const unsigned off = a_row[j] + (unsigned)min(k0 + a_k[j], K - 8) * 2u;
+      copy_to_lds(p.a, off, lds_addr(sa + (j * kWaves + wave) * 1024));
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadsB; ++j) {
+      const unsigned off = (unsigned)min(k0 + b_row[j], K - 1) * ldb + b_col[j];
+      copy_to_lds(p.b, off, lds_addr(sb + (j * kWaves + wave) * 1024));
+    }
+  };
+
+  f32x16_t acc[kMB][kNB];
+#pragma unroll
+  for (int i = 0; i < kMB; ++i)
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) acc[i][j] = f32x16_t{};
+
+  // LDS byte offsets of this lane's operands at k16 step 0 (step kc adds 2kc chunks of
+  // A, 16 rows of B).
+  unsigned a_op[kMB], b_op[kNB][2];
+#pragma unroll
+  for (int i = 0; i < kMB; ++i) a_op[i] = lds_off<8>(wave_m * (kMB * 32) + i * 32 + (lane & 31), G);
+#pragma unroll
+  for (int j = 0; j < kNB; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) b_op[j][h] = v_operand_off<32>(lane, wave_n * kNB + j, h);
+
+  auto compute = [&](const char* sa, const char* sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kc = 0; kc < kBK / 16; ++kc) {
+      v8_t af[kMB], bf[kNB];
+#pragma unroll
+      for (int i = 0; i < kMB; ++i) {
+        // chunk 2kc + G of the row: the R = 8 swizzle keeps chunk bits above bit 0 in
+        // the slot's low bits, so stepping kc moves the slot by XOR, not by addition
+        af[i] = *(const v8_t*)(sa + (a_op[i] ^ (unsigned)(kc << 5)));
+      }
+#pragma unroll
+      for (int j = 0; j < kNB; ++j) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(sb + b_op[j][0] + kc * 16 * (kBN * 2)));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(sb + b_op[j][1] + kc * 16 * (kBN * 2)));
+        bf[j] = __builtin_bit_cast(v8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) acc[i][j] = Mfma<T>::mma(bf[j], af[i], acc[i][j]);
+    }
+  };
+
+  auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_tag)::value;
+    char* sa = smem + buf * kStage;
+    wait_vmcnt<0>();
+    if (t * kBK + kBK > K) {
+      // ragged last k-step: zero the A chunks past K that this thread copied
+#pragma unroll
+      for (int j = 0; j < kLoadsA; ++j)
+        if (t * kBK + a_k[j] >= K) *(uint4*)(sa + (j * kWaves + wave) * 1024 + lane * 16) = uint4{0, 0, 0, 0};
+    }
+    tile_barrier();
+    if (t + 1 < nk) issue(t + 1, buf ^ 1);
+    compute(sa, sa + kATile);
+  };
+
+  issue(0, 0);
+  for (int t = 0; t < nk; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < nk) step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  // --- epilogue: register r of block (i, j) is row (lane & 31) of the block and
+  // column 32j + 16(r >> 3) + 8G + (r & 7).
+#pragma unroll
+  for (int i = 0; i < kMB; ++i) {
+    const int m = m0 + wave_m * (kMB * 32) + i * 32 + (lane & 31);
+    if (m >= M) continue;
+    T* crow = (T*)p.c + (size_t)m * N;
+#pragma unroll
+    for (int j = 0; j < kNB; ++j)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int n = n0 + wave_n * (kNB * 32) + j * 32 + 16 * hh + 8 * G;
+        if (n >= N) continue;
+        typename Mfma<T>::v8 ov;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ov[e] = (T)acc[i][j][8 * hh + e];
+        *(typename Mfma<T>::v8*)(crow + n) = ov;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const void* a, const void* b, void* c, int M, int N, int K, int dtype,
+                       hipStream_t stream) {
+  GemmParams p;
+  p.a = a;
+  p.b = b;
+  p.c = c;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.tiles_m = (M + kBM - 1) / kBM;
+  p.tiles_n = (N + kBN - 1) / kBN;
+  p.total = p.tiles_m * p.tiles_n;
+  if (dtype == 2)
+    hipLaunchKernelGGL(gemm_kernel<_Float16>, dim3(p.total), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_kernel<__bf16>, dim3(p.total), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mha_impl

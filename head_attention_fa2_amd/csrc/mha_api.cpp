@@ -118,6 +118,18 @@ mha_status validate_paged(const void* q, const void* k_pool, const void* v_pool,
   return MHA_OK;
 }
 
+mha_status validate_gemm(const void* a, const void* b, const void* c, int M, int N, int K, mha_dtype dtype) {
+  if (!a || !b || !c) return MHA_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1) return MHA_ERR_INVALID_ARG;
+  if (dtype != MHA_DTYPE_F32 && dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_F16) return MHA_ERR_INVALID_ARG;
+  if (dtype == MHA_DTYPE_F32) return MHA_ERR_UNSUPPORTED;
+  if (N % 8 != 0 || K % 8 != 0) return MHA_ERR_UNSUPPORTED;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return MHA_ERR_UNSUPPORTED;
+  // 32-bit byte offsets inside A and B; the tile count fits the grid
+  if ((int64_t)M * K * 2 > UINT32_MAX || (int64_t)K * N * 2 > UINT32_MAX) return MHA_ERR_UNSUPPORTED;
+  return MHA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,6 +221,24 @@ size_t mha_fwd_paged_workspace_size(int B, int H, int Nq, int d, int block_size,
 double mha_fwd_paged_bytes(int B, int H, int Nq, long long total_keys, int d, mha_dtype dtype) {
   const double elem = dtype == MHA_DTYPE_F32 ? 4.0 : 2.0;
   return (2.0 * B * Nq + 2.0 * (double)total_keys) * H * (double)d * elem + 4.0 * B * H * (double)Nq;
+}
+
+mha_status mha_gemm_validate(const void* a, const void* b, const void* c, int M, int N, int K, mha_dtype dtype) {
+  return validate_gemm(a, b, c, M, N, K, dtype);
+}
+
+mha_status mha_gemm(const void* a, const void* b, void* c, int M, int N, int K, mha_dtype dtype, void* stream) {
+  const mha_status st = validate_gemm(a, b, c, M, N, K, dtype);
+  if (st != MHA_OK) return st;
+  const hipError_t e = mha_impl::launch_gemm(a, b, c, M, N, K, (int)dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+double mha_gemm_flops(int M, int N, int K) { return 2.0 * M * (double)N * (double)K; }
+
+double mha_gemm_bytes(int M, int N, int K, mha_dtype dtype) {
+  const double elem = dtype == MHA_DTYPE_F32 ? 4.0 : 2.0;
+  return ((double)M * K + (double)K * N + (double)M * N) * elem;
 }
 
 double mha_fwd_splitkv_bytes(int B, int H, int Nq, int Nk, int d, mha_dtype dtype) {

@@ -30,6 +30,11 @@ hipError_t launch_fwd_paged(const void* q, const void* k_pool, const void* v_poo
                             int dtype, int num_blocks, int bs_log2, int max_blocks, int splits, int chunk,
                             float* part_o, float* part_lse, hipStream_t stream);
 
+// Enqueue the dense GEMM C [M,N] = A [M,K] . B [K,N] (row-major, dtype 1 bf16 or 2 fp16,
+// float32 accumulation, C in the input type).  Arguments validated.
+hipError_t launch_gemm(const void* a, const void* b, void* c, int M, int N, int K, int dtype,
+                       hipStream_t stream);
+
 }  // namespace mha_impl
 
 #endif  // MHA_LAUNCH_H_

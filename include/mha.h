@@ -229,6 +229,42 @@ mha_status mha_fwd_paged_validate(const void* q, const void* k_pool, const void*
  */
 double mha_fwd_paged_bytes(int B, int H, int Nq, long long total_keys, int d, mha_dtype dtype);
 
+/*
+ * Dense GEMM.
+ *
+ * The tiled contraction of the ML-Triton paper, section 2 (a workgroup accumulates its
+ * block of C over k-steps in float32 and stores it once) and section 4.1 (compute-bound
+ * GEMMs from LLM layers):
+ *
+ *     C[m][n] = sum_k A[m][k] * B[k][n]
+ *
+ *   a       [M, K] row-major, b [K, N] row-major, c [M, N] row-major (device pointers),
+ *           all of `dtype`: MHA_DTYPE_BF16 or MHA_DTYPE_F16.  Products are accumulated
+ *           in float32 and C is rounded once to `dtype` (round to nearest even).  C
+ *           must not overlap A or B.
+ *   M, N, K >= 1; N and K multiples of 8 (16-byte rows); A and B under 4 GiB each.
+ *   stream  hipStream_t (NULL = default stream); one kernel is enqueued.
+ *
+ * Errors: MHA_ERR_INVALID_ARG for a null pointer, a size < 1 or an unknown dtype;
+ * MHA_ERR_UNSUPPORTED for fp32, N or K not a multiple of 8, a pointer not 16-byte
+ * aligned, or an operand of 4 GiB or more; MHA_ERR_HIP if the launch fails.
+ */
+mha_status mha_gemm(const void* a, const void* b, void* c, int M, int N, int K, mha_dtype dtype,
+                    void* stream);
+
+/* mha_gemm_validate -- the argument checks of mha_gemm alone, host only. */
+mha_status mha_gemm_validate(const void* a, const void* b, const void* c, int M, int N, int K,
+                             mha_dtype dtype);
+
+/* mha_gemm_flops -- 2*M*N*K, the credited work of one mha_gemm call.  Host only. */
+double mha_gemm_flops(int M, int N, int K);
+
+/*
+ * mha_gemm_bytes -- algorithmic HBM traffic of one mha_gemm call: A and B read once,
+ * C written once.  Host only.
+ */
+double mha_gemm_bytes(int M, int N, int K, mha_dtype dtype);
+
 /* mha_status_string -- static, human-readable text for a status code. */
 const char* mha_status_string(mha_status status);
 

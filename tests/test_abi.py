@@ -190,3 +190,21 @@ def test_paged_bytes():
     assert mha.mha_fwd_paged_bytes(64, 8, 1, 263473, 128, BF16) == \
         (2 * 64 + 2 * 263473) * 8 * 128 * 2 + 4 * 64 * 8
     assert mha.mha_fwd_paged_bytes(2, 3, 4, 5, 64, F32) == (2 * 2 * 4 + 2 * 5) * 3 * 64 * 4 + 4 * 2 * 3 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(dtype=F16), OK), (dict(M=1, N=8, K=8), OK),
+    (dict(a=0), INVALID), (dict(c=0), INVALID), (dict(M=0), INVALID), (dict(K=-8), INVALID), (dict(dtype=7), INVALID),
+    (dict(dtype=F32), UNSUPPORTED), (dict(N=12), UNSUPPORTED), (dict(K=100), UNSUPPORTED),
+    (dict(b=P + 8), UNSUPPORTED), (dict(M=1 << 20, K=4096), UNSUPPORTED), (dict(N=1 << 19, K=8192), UNSUPPORTED),
+])
+def test_gemm_validate(kw, code):
+    a = dict(a=P, b=P, c=P, M=1000, N=4096, K=4096, dtype=BF16)
+    a.update(kw)
+    assert mha.mha_gemm_validate(a["a"], a["b"], a["c"], a["M"], a["N"], a["K"], a["dtype"]) == code
+
+
+def test_gemm_rejects_before_launch_and_accounting():
+    assert mha.mha_gemm(P, P, 0, 8, 8, 8, BF16, 0) == INVALID
+    assert mha.mha_gemm_flops(1024, 4096, 14336) == 2.0 * 1024 * 4096 * 14336
+    assert mha.mha_gemm_bytes(1024, 4096, 14336, BF16) == (1024 * 14336 + 14336 * 4096 + 1024 * 4096) * 2
