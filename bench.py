@@ -29,7 +29,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X published
 HBM_GBS = 8000.0
 
 
-KERNEL_SOURCES = ("mha_fwd_kernel.hip", "mha_layout.h", "mha_launch.h")
+KERNEL_SOURCES = ("mha_fwd_kernel.hip", "mha_layout.h", "gfx950_lds.h")
 
 
 def kernel_source_sha256() -> str:
