@@ -1,9 +1,9 @@
 """GPU parity of the dense GEMM (mha_gemm): C = A.B compared element by element with the
 CPU oracle's float64 product, within the oracle's bound for a float32-accumulated,
-once-rounded result (u_out |C| + gamma_K |A||B|, bf16 u = 2^-8, fp16 u = 2^-11).  Small
-shapes cover ragged M, N and K (several 256 x 256 tiles, partial tiles, K not a
-multiple of the 64-wide k-step); the full-size workloads are checked on sampled rows
-and columns."""
+once-rounded result (u_out |C| + gamma_K |A||B|, bf16 u = 2^-8, fp16 u = 2^-11).  The
+element-wise shapes cover ragged M, N and K (partial tiles, K not a multiple of the
+64-wide k-step) under both tilings (128 x 128 below 192 tiles of 256 x 256, 256 x 256
+from there); the full-size workloads are checked on sampled rows and columns."""
 import numpy as np
 import pytest
 import torch
@@ -38,6 +38,8 @@ CASES = [
     (1, 8, 8, "bf16"), (256, 256, 64, "bf16"), (300, 520, 200, "bf16"), (512, 768, 1024, "bf16"),
     (33, 1000, 72, "f16"), (777, 264, 136, "bf16"), (1024, 1024, 8, "f16"), (257, 2056, 640, "f16"),
     (2048, 256, 4104, "bf16"), (96, 64, 4096, "bf16"),
+    # 208 tiles of 256 x 256: the large tiling, ragged in M, N and K
+    (4000, 3080, 1000, "bf16"), (3900, 3336, 264, "f16"),
 ]
 
 
