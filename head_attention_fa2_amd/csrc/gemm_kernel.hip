@@ -19,7 +19,8 @@
 //    columns in one lane.
 //  * k-steps of 64: the A (256 x 64) and B (64 x 256) tiles are copied HBM -> LDS with
 //    global_load_lds_dwordx4, double buffered with one barrier per k-step (the copy of
-//    step t+1 is in flight while step t is consumed).  LDS rows are XOR-swizzled in
+//    step t+1 is in flight while step t is consumed; its A and B parts are issued after
+//    the first and the second 16-wide substep of step t).  LDS rows are XOR-swizzled in
 //    16-byte chunks so that both operand reads are free of bank conflicts.
 //  * Workgroup ids are renumbered so that each XCD gets a contiguous range of tiles,
 //    traversed in groups of 8 block-rows (the grouped order of the Triton tutorial's
@@ -150,10 +151,36 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
   }
   const int nk = (K + kBK - 1) / kBK;
 
-  auto issue = [&](int t, int buf) __attribute__((always_inline)) {
+  // full k-steps: uniform (SGPR) bases advanced by k0 and per-lane offsets fixed for
+  // the whole loop, so a copy costs no vector arithmetic
+  unsigned a_off[kLoadsA], b_off[kLoadsB];
+#pragma unroll
+  for (int j = 0; j < kLoadsA; ++j) a_off[j] = a_row[j] + (unsigned)a_k[j] * 2u;
+#pragma unroll
+  for (int j = 0; j < kLoadsB; ++j) b_off[j] = (unsigned)b_row[j] * ldb + b_col[j];
+
+  // Copies of k-step t into buffer buf: the A tile (kA), the B tile (kB) or both.  A
+  // ragged last k-step is issued whole with the A part.
+  constexpr int kA = 1, kB = 2;
+  auto issue = [&](int t, int buf, int parts) __attribute__((always_inline)) {
     const int k0 = t * kBK;
     char* sa = smem + buf * kStage;
     char* sb = sa + kATile;
+    if (k0 + kBK <= K) {
+      const char* ga = (const char*)p.a + (size_t)k0 * 2;
+      const char* gb = (const char*)p.b + (size_t)k0 * ldb;
+      if (parts & kA) {
+#pragma unroll
+        for (int j = 0; j < kLoadsA; ++j) copy_to_lds(ga, a_off[j], lds_addr(sa + (j * kWaves + wave) * 1024));
+      }
+      if (parts & kB) {
+#pragma unroll
+        for (int j = 0; j < kLoadsB; ++j) copy_to_lds(gb, b_off[j], lds_addr(sb + (j * kWaves + wave) * 1024));
+      }
+      return;
+    }
+    if (!(parts & kA)) return;
+    // ragged last k-step: clamped offsets from the row bases
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
       // chunks past K read the last chunk of the row; zeroed after they land
@@ -183,9 +210,10 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) b_op[j][h] = v_operand_off<kRB>(lane, wave_n * kNB + j, h);
 
-  auto compute = [&](const char* sa, const char* sb) __attribute__((always_inline)) {
+  // k16 substeps [kc_lo, kc_hi) of a k-step
+  auto compute = [&](const char* sa, const char* sb, int kc_lo, int kc_hi) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kc = 0; kc < kBK / 16; ++kc) {
+    for (int kc = kc_lo; kc < kc_hi; ++kc) {
       v8_t af[kMB], bf[kNB];
 #pragma unroll
       for (int i = 0; i < kMB; ++i) {
@@ -219,11 +247,16 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
         if (t * kBK + a_k[j] >= K) *(uint4*)(sa + (j * kWaves + wave) * 1024 + lane * 16) = uint4{0, 0, 0, 0};
     }
     tile_barrier();
-    if (t + 1 < nk) issue(t + 1, buf ^ 1);
-    compute(sa, sa + kATile);
+    // the next step's copies go out between the first MFMAs of this one (measured: up
+    // to a quarter faster than issuing them all before the first MFMA)
+    compute(sa, sa + kATile, 0, 1);
+    if (t + 1 < nk) issue(t + 1, buf ^ 1, kA);
+    compute(sa, sa + kATile, 1, 2);
+    if (t + 1 < nk) issue(t + 1, buf ^ 1, kB);
+    compute(sa, sa + kATile, 2, kBK / 16);
   };
 
-  issue(0, 0);
+  issue(0, 0, kA | kB);
   for (int t = 0; t < nk; t += 2) {
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < nk) step(t + 1, std::integral_constant<int, 1>{});
