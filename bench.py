@@ -181,6 +181,38 @@ def time_gemm(w, steps, warmup, dev, torch_too=True):
     return dict(ms=ms, ms_torch=ms_torch, inputs=(a, b), out=c)
 
 
+def time_gemm_splitk(w, steps, warmup, dev):
+    """Time mha.gemm_splitk (library split count) and torch.matmul on a memory-bound GEMM."""
+    import torch
+
+    import head_attention_fa2_amd as mha
+    import mha_inputs
+
+    a, b = mha_inputs.draw_gemm(w.M, w.N, w.K, w.dtype, w.seed)
+    ta, tb = _to_device(a, w.dtype, dev), _to_device(b, w.dtype, dev)
+    c = torch.empty((w.M, w.N), dtype=ta.dtype, device=dev)
+    ws = torch.empty(mha.mha_gemm_splitk_workspace_size(w.M, w.N, w.K, 0), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize(dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize(dev)
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    ms_plain = timed(lambda: mha.gemm(ta, tb, out=c, stream=stream))
+    ms_torch = timed(lambda: torch.matmul(ta, tb, out=c))
+    ms = timed(lambda: mha.gemm_splitk(ta, tb, out=c, workspace=ws, stream=stream))
+    torch.cuda.synchronize(dev)
+    return dict(ms=ms, ms_plain=ms_plain, ms_torch=ms_torch, inputs=(a, b), out=c)
+
+
 def parity_sample_gemm(w, inputs, out, n=8):
     """Largest error / bound over sampled entries of C (<= 1 passes)."""
     import numpy as np
@@ -388,6 +420,19 @@ def main():
             print(json.dumps({"workload": name, "M": ww.M, "N": ww.N, "K": ww.K, "ms": round(rr["ms"], 5),
                               "TFLOP/s": round(tf, 1), "pct_of_peak": round(100 * tf / PEAK_TFLOPS[ww.dtype], 2),
                               "torch_matmul_TFLOP/s": round(tft, 1), "vs_torch": round(tf / tft, 3),
+                              "parity": parity_sample_gemm(ww, rr["inputs"], rr["out"])}),
+                  file=sys.stderr, flush=True)
+            del rr
+    if args.gemm:
+        for name, ww in mha_inputs.GEMM_MEMBOUND.items():
+            rr = time_gemm_splitk(ww, max(10, args.steps // 4), 5, dev)
+            nbytes = mha.mha_gemm_bytes(ww.M, ww.N, ww.K, {"bf16": 1, "f16": 2}[ww.dtype])
+            gbs = nbytes / (rr["ms"] * 1e-3) / 1e9
+            print(json.dumps({"workload": name, "M": ww.M, "N": ww.N, "K": ww.K,
+                              "splits": mha.mha_gemm_splitk_splits(ww.M, ww.N, ww.K, 0), "ms": round(rr["ms"], 5),
+                              "GB/s": round(gbs, 1), "pct_of_hbm": round(100 * gbs / HBM_GBS, 2),
+                              "plain_gemm_GB/s": round(nbytes / (rr["ms_plain"] * 1e-3) / 1e9, 1),
+                              "torch_matmul_GB/s": round(nbytes / (rr["ms_torch"] * 1e-3) / 1e9, 1),
                               "parity": parity_sample_gemm(ww, rr["inputs"], rr["out"])}),
                   file=sys.stderr, flush=True)
             del rr

@@ -6,10 +6,12 @@ the C ABI of ``include/mha.h``).  This module only marshals arguments: the funct
 ``mha_fwd_splitkv``, ``mha_fwd_splitkv_validate``, ``mha_fwd_splitkv_splits``,
 ``mha_fwd_splitkv_workspace_size``, ``mha_fwd_splitkv_bytes``, ``mha_fwd_paged``,
 ``mha_fwd_paged_validate``, ``mha_fwd_paged_splits``, ``mha_fwd_paged_workspace_size``,
-``mha_fwd_paged_bytes``, ``mha_gemm``, ``mha_gemm_validate``, ``mha_gemm_flops``,
-``mha_gemm_bytes``, ``mha_status_string`` and ``mha_version`` mirror the C entry points
-one to one, and :func:`fwd` / :func:`fwd_splitkv` / :func:`fwd_paged` / :func:`gemm` are
-the PyTorch-facing conveniences (device memory and the stream
+``mha_fwd_paged_bytes``, ``mha_gemm``, ``mha_gemm_validate``, ``mha_gemm_splitk``,
+``mha_gemm_splitk_validate``, ``mha_gemm_splitk_splits``, ``mha_gemm_splitk_workspace_size``,
+``mha_gemm_flops``, ``mha_gemm_bytes``, ``mha_status_string`` and ``mha_version`` mirror
+the C entry points one to one, and :func:`fwd` / :func:`fwd_splitkv` / :func:`fwd_paged` /
+:func:`gemm` / :func:`gemm_splitk` are the PyTorch-facing conveniences (device memory
+and the stream
 come from torch; nothing is computed in Python).  There is no fallback: if the library is not
 built or a call fails, an exception is raised.
 """
@@ -26,8 +28,9 @@ __all__ = [
     "mha_fwd_bytes", "mha_fwd_splitkv", "mha_fwd_splitkv_validate", "mha_fwd_splitkv_splits",
     "mha_fwd_splitkv_workspace_size", "mha_fwd_splitkv_bytes", "mha_fwd_paged", "mha_fwd_paged_validate",
     "mha_fwd_paged_splits", "mha_fwd_paged_workspace_size", "mha_fwd_paged_bytes", "mha_status_string",
-    "mha_version", "mha_gemm", "mha_gemm_validate", "mha_gemm_flops", "mha_gemm_bytes",
-    "fwd", "fwd_splitkv", "fwd_paged", "gemm", "MhaError",
+    "mha_version", "mha_gemm", "mha_gemm_validate", "mha_gemm_splitk", "mha_gemm_splitk_validate",
+    "mha_gemm_splitk_splits", "mha_gemm_splitk_workspace_size", "mha_gemm_flops", "mha_gemm_bytes",
+    "fwd", "fwd_splitkv", "fwd_paged", "gemm", "gemm_splitk", "MhaError",
 ]
 
 MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_HIP = 0, 1, 2, 3
@@ -92,6 +95,14 @@ def load() -> ctypes.CDLL:
     lib.mha_gemm.restype = i
     lib.mha_gemm_validate.argtypes = [vp, vp, vp, i, i, i, i]
     lib.mha_gemm_validate.restype = i
+    lib.mha_gemm_splitk.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.mha_gemm_splitk.restype = i
+    lib.mha_gemm_splitk_validate.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz]
+    lib.mha_gemm_splitk_validate.restype = i
+    lib.mha_gemm_splitk_splits.argtypes = [i, i, i, i]
+    lib.mha_gemm_splitk_splits.restype = i
+    lib.mha_gemm_splitk_workspace_size.argtypes = [i, i, i, i]
+    lib.mha_gemm_splitk_workspace_size.restype = sz
     lib.mha_gemm_flops.argtypes = [i, i, i]
     lib.mha_gemm_flops.restype = ctypes.c_double
     lib.mha_gemm_bytes.argtypes = [i, i, i, i]
@@ -190,6 +201,25 @@ def mha_gemm(a: int, b: int, c: int, M: int, N: int, K: int, dtype: int, stream:
 
 def mha_gemm_validate(a: int, b: int, c: int, M: int, N: int, K: int, dtype: int) -> int:
     return load().mha_gemm_validate(a, b, c, M, N, K, dtype)
+
+
+def mha_gemm_splitk(a: int, b: int, c: int, M: int, N: int, K: int, dtype: int, splits: int, workspace: int,
+                    workspace_bytes: int, stream: int) -> int:
+    """Enqueue the split-K C = A.B (partials, then their sum) on ``stream``."""
+    return load().mha_gemm_splitk(a, b, c, M, N, K, dtype, splits, workspace, workspace_bytes, stream)
+
+
+def mha_gemm_splitk_validate(a: int, b: int, c: int, M: int, N: int, K: int, dtype: int, splits: int,
+                             workspace: int, workspace_bytes: int) -> int:
+    return load().mha_gemm_splitk_validate(a, b, c, M, N, K, dtype, splits, workspace, workspace_bytes)
+
+
+def mha_gemm_splitk_splits(M: int, N: int, K: int, splits: int) -> int:
+    return load().mha_gemm_splitk_splits(M, N, K, splits)
+
+
+def mha_gemm_splitk_workspace_size(M: int, N: int, K: int, splits: int) -> int:
+    return load().mha_gemm_splitk_workspace_size(M, N, K, splits)
 
 
 def mha_gemm_flops(M: int, N: int, K: int) -> float:
@@ -385,6 +415,43 @@ def gemm(a, b, out=None, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(a.device)
     st = mha_gemm(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, _DTYPES[a.dtype], stream.cuda_stream)
+    if st != MHA_OK:
+        raise MhaError(st)
+    return out
+
+
+def gemm_splitk(a, b, splits: int = 0, out=None, workspace=None, stream=None):
+    """``C = gemm_splitk(a, b)``: as :func:`gemm`, with K cut into ``splits`` ranges (0:
+    the library's choice) whose float32 partials are then summed; for shapes with one
+    small dimension.  ``workspace`` (a CUDA tensor of at least
+    :func:`mha_gemm_splitk_workspace_size` bytes) is allocated through torch when not given.
+    """
+    import torch
+
+    _DTYPES = {torch.bfloat16: MHA_DTYPE_BF16, torch.float16: MHA_DTYPE_F16}
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("need a [M, K] and b [K, N]")
+    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
+        raise ValueError("a and b must be on the same GPU")
+    if a.dtype not in _DTYPES or b.dtype != a.dtype:
+        raise ValueError("a and b must both be bfloat16 or both float16")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous")
+    M, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    elif out.shape != (M, N) or out.dtype != a.dtype or out.device != a.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] tensor like a")
+    need = mha_gemm_splitk_workspace_size(M, N, K, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    elif not workspace.is_cuda or workspace.device != a.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor on a's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    st = mha_gemm_splitk(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, _DTYPES[a.dtype], int(splits),
+                         workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream.cuda_stream)
     if st != MHA_OK:
         raise MhaError(st)
     return out

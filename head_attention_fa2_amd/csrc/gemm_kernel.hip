@@ -51,6 +51,7 @@ using mha_layout::v_operand_off;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -100,10 +101,17 @@ struct GemmParams {
   const void* b;
   void* c;
   int M, N, K;
-  int tiles_m, tiles_n, total;
+  int tiles_m, tiles_n, total;   // total: tiles of C
+  // split-K only: K per split (a multiple of the k-step), splits, float32 partial
+  // products [splits][M][N]
+  int kchunk = 0;
+  int splits = 1;
+  float* part = nullptr;
 };
 
-template <typename T, typename C>
+// SPLITK: workgroup (split, tile) sums k in [split*kchunk, min(K, (split+1)*kchunk))
+// and stores its float32 partial block; gemm_splitk_reduce adds the partials.
+template <typename T, typename C, bool SPLITK = false>
 __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
   typedef typename Mfma<T>::v8 v8_t;
   constexpr int kBM = C::BM, kBN = C::BN, kBK = C::BK, kWaves = C::Waves, kWavesN = C::WN;
@@ -117,8 +125,15 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
   const int G = lane >> 5;
 
   // --- workgroup -> tile: contiguous id ranges per XCD, grouped block-row order.
+  const int grid = SPLITK ? p.total * p.splits : p.total;
   int id = blockIdx.x;
-  if ((p.total & 7) == 0) id = (id & 7) * (p.total >> 3) + (id >> 3);
+  if ((grid & 7) == 0) id = (id & 7) * (grid >> 3) + (id >> 3);
+  int kbeg = 0;
+  if constexpr (SPLITK) {
+    const int split = id / p.total;
+    id -= split * p.total;
+    kbeg = split * p.kchunk;
+  }
   const int group = kGroupM * p.tiles_n;
   const int first_m = id / group * kGroupM;
   const int gsize = min(p.tiles_m - first_m, kGroupM);
@@ -149,7 +164,8 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
     b_row[j] = r;
     b_col[j] = (unsigned)min(n0 / 8 + c, N / 8 - 1) * 16u;
   }
-  const int nk = (K + kBK - 1) / kBK;
+  const int kend = SPLITK ? min(K, kbeg + p.kchunk) : K;
+  const int nk = (kend - kbeg + kBK - 1) / kBK;
 
   // full k-steps: uniform (SGPR) bases advanced by k0 and per-lane offsets fixed for
   // the whole loop, so a copy costs no vector arithmetic
@@ -163,7 +179,7 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
   // ragged last k-step is issued whole with the A part.
   constexpr int kA = 1, kB = 2;
   auto issue = [&](int t, int buf, int parts) __attribute__((always_inline)) {
-    const int k0 = t * kBK;
+    const int k0 = kbeg + t * kBK;
     char* sa = smem + buf * kStage;
     char* sb = sa + kATile;
     if (k0 + kBK <= K) {
@@ -240,11 +256,12 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
     constexpr int buf = decltype(buf_tag)::value;
     char* sa = smem + buf * kStage;
     wait_vmcnt<0>();
-    if (t * kBK + kBK > K) {
+    const int k0 = kbeg + t * kBK;
+    if (k0 + kBK > K) {
       // ragged last k-step: zero the A chunks past K that this thread copied
 #pragma unroll
       for (int j = 0; j < kLoadsA; ++j)
-        if (t * kBK + a_k[j] >= K) *(uint4*)(sa + (j * kWaves + wave) * 1024 + lane * 16) = uint4{0, 0, 0, 0};
+        if (k0 + a_k[j] >= K) *(uint4*)(sa + (j * kWaves + wave) * 1024 + lane * 16) = uint4{0, 0, 0, 0};
     }
     tile_barrier();
     // the next step's copies go out between the first MFMAs of this one (measured: up
@@ -264,6 +281,31 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
 
   // --- epilogue: register r of block (i, j) is row (lane & 31) of the block and
   // column 32j + 16(r >> 3) + 8G + (r & 7).
+  if constexpr (SPLITK) {
+    // float32 partial block of this split
+    const int split = kbeg / p.kchunk;
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) {
+      const int m = m0 + wave_m * (kMB * 32) + i * 32 + (lane & 31);
+      if (m >= M) continue;
+      float* prow = p.part + ((size_t)split * M + m) * N;
+#pragma unroll
+      for (int j = 0; j < kNB; ++j)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int n = n0 + wave_n * (kNB * 32) + j * 32 + 16 * hh + 8 * G;
+          if (n >= N) continue;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            f32x4_t v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][8 * hh + 4 * q + e];
+            *(f32x4_t*)(prow + n + 4 * q) = v;
+          }
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kMB; ++i) {
     const int m = m0 + wave_m * (kMB * 32) + i * 32 + (lane & 31);
@@ -281,6 +323,29 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
         *(typename Mfma<T>::v8*)(crow + n) = ov;
       }
   }
+}
+
+// C = sum over splits of the float32 partials, rounded once to T.  Thread i owns the 8
+// consecutive elements 8i .. 8i+7 of C (N is a multiple of 8, so they share a row).
+constexpr int kReduceThreads = 256;
+template <typename T>
+__global__ __launch_bounds__(kReduceThreads) void gemm_splitk_reduce(GemmParams p) {
+  const size_t total = (size_t)p.M * p.N;
+  const size_t i = ((size_t)blockIdx.x * kReduceThreads + threadIdx.x) * 8;
+  if (i >= total) return;
+  f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.splits; ++s) {
+    const float* src = p.part + (size_t)s * total + i;
+    lo += *(const f32x4_t*)src;
+    hi += *(const f32x4_t*)(src + 4);
+  }
+  typename Mfma<T>::v8 ov;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ov[e] = (T)lo[e];
+    ov[4 + e] = (T)hi[e];
+  }
+  *(typename Mfma<T>::v8*)((T*)p.c + i) = ov;
 }
 
 template <typename C>
@@ -315,6 +380,37 @@ hipError_t launch_gemm(const void* a, const void* b, void* c, int M, int N, int 
     launch_tiled<Small>(p, dtype, stream);
   else
     launch_tiled<Large>(p, dtype, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_splitk(const void* a, const void* b, void* c, int M, int N, int K, int dtype, int splits,
+                              int kchunk, float* part, hipStream_t stream) {
+  GemmParams p;
+  p.a = a;
+  p.b = b;
+  p.c = c;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.kchunk = kchunk;
+  p.splits = splits;
+  p.part = part;
+  p.tiles_m = (M + Small::BM - 1) / Small::BM;
+  p.tiles_n = (N + Small::BN - 1) / Small::BN;
+  p.total = p.tiles_m * p.tiles_n;
+  const dim3 grid(p.total * splits);
+  const dim3 rgrid((unsigned)(((size_t)M * N / 8 + kReduceThreads - 1) / kReduceThreads));
+  if (dtype == 2) {
+    hipLaunchKernelGGL((gemm_kernel<_Float16, Small, true>), grid, dim3(Small::Threads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_splitk_reduce<_Float16>), rgrid, dim3(kReduceThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<__bf16, Small, true>), grid, dim3(Small::Threads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_splitk_reduce<__bf16>), rgrid, dim3(kReduceThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

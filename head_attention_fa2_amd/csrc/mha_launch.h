@@ -35,6 +35,11 @@ hipError_t launch_fwd_paged(const void* q, const void* k_pool, const void* v_poo
 hipError_t launch_gemm(const void* a, const void* b, void* c, int M, int N, int K, int dtype,
                        hipStream_t stream);
 
+// Enqueue the split-K GEMM: `splits` ranges of `kchunk` keys of K (a multiple of 64),
+// float32 partials in part [splits][M][N], then their sum rounded to C.  Validated.
+hipError_t launch_gemm_splitk(const void* a, const void* b, void* c, int M, int N, int K, int dtype, int splits,
+                              int kchunk, float* part, hipStream_t stream);
+
 }  // namespace mha_impl
 
 #endif  // MHA_LAUNCH_H_

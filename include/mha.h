@@ -256,6 +256,41 @@ mha_status mha_gemm(const void* a, const void* b, void* c, int M, int N, int K, 
 mha_status mha_gemm_validate(const void* a, const void* b, const void* c, int M, int N, int K,
                              mha_dtype dtype);
 
+/*
+ * Split-K GEMM, for the memory-bound shapes of the ML-Triton paper's section 4.1 (one
+ * small dimension, as in next-token prediction, where the tiles of C alone cannot
+ * occupy the GPU).  The same C = A.B as mha_gemm (same arguments and errors); K is cut
+ * into `splits` ranges, each workgroup accumulates one range of one 128 x 128 block of C
+ * in float32, and a second kernel adds the float32 partials and rounds the sum once to
+ * `dtype`.  The result is within the same bound as mha_gemm's (a float32-accumulated,
+ * once-rounded sum), summed in a different order.
+ *
+ *   splits      K ranges; 0 = automatic (mha_gemm_splitk_splits: the largest power of
+ *               two within about 512 workgroups and at least 4 steps of 64 per range;
+ *               the ranges are whole steps, so fewer may remain non-empty).
+ *   workspace, workspace_bytes
+ *               caller-owned device memory of at least mha_gemm_splitk_workspace_size(...)
+ *               bytes, 16-byte aligned, for the partials [splits][M][N] float32 (scratch;
+ *               calls that share it must not overlap in time).
+ *
+ * Errors as for mha_gemm, plus MHA_ERR_INVALID_ARG for splits < 0 or a null or too small
+ * workspace, MHA_ERR_UNSUPPORTED for a workspace not 16-byte aligned or M*N >= 2^31.
+ * Two kernels are enqueued on `stream`.
+ */
+mha_status mha_gemm_splitk(const void* a, const void* b, void* c, int M, int N, int K, mha_dtype dtype,
+                           int splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* mha_gemm_splitk_validate -- the argument checks of mha_gemm_splitk alone, host only. */
+mha_status mha_gemm_splitk_validate(const void* a, const void* b, const void* c, int M, int N, int K,
+                                    mha_dtype dtype, int splits, const void* workspace,
+                                    size_t workspace_bytes);
+
+/* mha_gemm_splitk_splits -- K ranges mha_gemm_splitk uses for a request; 0 if invalid. */
+int mha_gemm_splitk_splits(int M, int N, int K, int splits);
+
+/* mha_gemm_splitk_workspace_size -- resolved_splits * M * N * 4 bytes; 0 if invalid. */
+size_t mha_gemm_splitk_workspace_size(int M, int N, int K, int splits);
+
 /* mha_gemm_flops -- 2*M*N*K, the credited work of one mha_gemm call.  Host only. */
 double mha_gemm_flops(int M, int N, int K);
 

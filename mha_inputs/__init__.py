@@ -31,6 +31,7 @@ __all__ = [
     "PAGED",
     "GemmWorkload",
     "GEMM",
+    "GEMM_MEMBOUND",
     "draw_gemm",
     "f32_to_bf16_bits",
     "f32_to_f16_bits",
@@ -219,6 +220,20 @@ for _i, ((_k, _n), _m) in enumerate(((kn, m) for kn in ((4096, 4096), (4096, 143
                                      for m in (1024, 2048, 4096, 8192, 16384))):
     _g = GemmWorkload(f"bf16_gemm_M{_m}_N{_n}_K{_k}", _m, _n, _k, "bf16", seed=400 + _i)
     GEMM[_g.name] = _g
+
+
+# Memory-bound GEMMs (section 4.1, Figure 12): the pages keep "large m, large k and large
+# n" and the next-token stage.  One large dimension at a time against Llama-3-8B sizes:
+# a 64-way router over 64k tokens (large M), and 16 decoding tokens through the MLP up
+# (large N) and down (large K) projections.
+GEMM_MEMBOUND: Dict[str, GemmWorkload] = {
+    g.name: g
+    for g in [
+        GemmWorkload("bf16_gemm_M65536_N64_K4096", 65536, 64, 4096, "bf16", seed=450),
+        GemmWorkload("bf16_gemm_M16_N14336_K4096", 16, 14336, 4096, "bf16", seed=451),
+        GemmWorkload("bf16_gemm_M16_N4096_K14336", 16, 4096, 14336, "bf16", seed=452),
+    ]
+}
 
 
 def _sample(rng: np.random.Generator, shape, dist: Dist) -> np.ndarray:

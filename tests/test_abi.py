@@ -208,3 +208,35 @@ def test_gemm_rejects_before_launch_and_accounting():
     assert mha.mha_gemm(P, P, 0, 8, 8, 8, BF16, 0) == INVALID
     assert mha.mha_gemm_flops(1024, 4096, 14336) == 2.0 * 1024 * 4096 * 14336
     assert mha.mha_gemm_bytes(1024, 4096, 14336, BF16) == (1024 * 14336 + 14336 * 4096 + 1024 * 4096) * 2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(splits=3), OK), (dict(dtype=F16, M=1, N=8, K=8), OK),
+    (dict(ws=0), INVALID), (dict(wsb=16), INVALID), (dict(splits=-2), INVALID), (dict(a=0), INVALID),
+    (dict(ws=P + 4), UNSUPPORTED), (dict(K=12), UNSUPPORTED), (dict(dtype=F32), UNSUPPORTED),
+])
+def test_gemm_splitk_validate(kw, code):
+    a = dict(a=P, b=P, c=P, M=16, N=4096, K=14336, dtype=BF16, splits=0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    assert mha.mha_gemm_splitk_validate(a["a"], a["b"], a["c"], a["M"], a["N"], a["K"], a["dtype"], a["splits"],
+                                        a["ws"], a["wsb"]) == code
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (16, 14336, 4096), (16, 4096, 14336), (65536, 64, 4096),
+                                   (300, 520, 200), (128, 128, 65536), (16, 1000, 4104)])
+@pytest.mark.parametrize("splits", [0, 1, 3, 100000])
+def test_gemm_splitk_partition(M, N, K, splits):
+    s = mha.mha_gemm_splitk_splits(M, N, K, splits)
+    steps = -(-K // 64)
+    assert 1 <= s <= steps
+    if splits > 0:
+        assert s <= splits
+    else:
+        tiles = -(-M // 128) * -(-N // 128)
+        want = min(-(-512 // tiles), (steps + 3) // 4)
+        p2 = 1
+        while p2 * 2 <= want:
+            p2 *= 2
+        assert s == -(-steps // -(-steps // p2))       # ranges of ceil(steps / p2) steps
+    assert mha.mha_gemm_splitk_workspace_size(M, N, K, splits) == s * M * N * 4
+    assert mha.mha_gemm_splitk(P, P, P, M, N, K, BF16, splits, 0, 0, 0) == INVALID

@@ -96,3 +96,50 @@ def test_gemm_errors_raise():
         mha.gemm(a, b[:8])
     with pytest.raises(ValueError):
         mha.gemm(a.float(), b.float())
+
+
+SPLITK_CASES = [
+    # (M, N, K, dtype, splits)
+    (1, 8, 8, "bf16", 0), (16, 1000, 4104, "bf16", 0), (33, 264, 1000, "f16", 3), (300, 520, 200, "bf16", 2),
+    (16, 4096, 2048, "bf16", 7), (129, 136, 8192, "f16", 0), (2, 64, 640, "bf16", 100),
+]
+
+
+@pytest.mark.parametrize("M,N,K,dtype,splits", SPLITK_CASES)
+def test_gemm_splitk_elementwise(M, N, K, dtype, splits):
+    a_bits, b_bits = mha_inputs.draw_gemm(M, N, K, dtype, seed=M * 3 + N + K + splits)
+    ta, tb = gu.to_device(a_bits, dtype), gu.to_device(b_bits, dtype)
+    c = mha.gemm_splitk(ta, tb, splits=splits)
+    torch.cuda.synchronize()
+    used = mha.mha_gemm_splitk_splits(M, N, K, splits)
+    _check(c.float().cpu().numpy().astype(np.float64), oracle.decode(a_bits, dtype), oracle.decode(b_bits, dtype),
+           dtype, f"gemm_splitk M{M} N{N} K{K} {dtype} splits={splits} (used {used})")
+
+
+def test_gemm_splitk_workspace_reused():
+    ws = torch.empty(mha.mha_gemm_splitk_workspace_size(64, 2048, 4096, 8), dtype=torch.uint8, device="cuda")
+    for (M, N, K, splits) in ((64, 2048, 4096, 8), (16, 520, 1000, 3)):
+        a_bits, b_bits = mha_inputs.draw_gemm(M, N, K, "bf16", seed=K + N)
+        c = mha.gemm_splitk(gu.to_device(a_bits, "bf16"), gu.to_device(b_bits, "bf16"), splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        _check(c.float().cpu().numpy().astype(np.float64), oracle.decode(a_bits, "bf16"),
+               oracle.decode(b_bits, "bf16"), "bf16", f"shared workspace M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("name", list(mha_inputs.GEMM_MEMBOUND))
+def test_gemm_membound_workload(name):
+    w = mha_inputs.GEMM_MEMBOUND[name]
+    a_bits, b_bits = mha_inputs.draw_gemm(w.M, w.N, w.K, w.dtype, w.seed)
+    ta, tb = gu.to_device(a_bits, w.dtype), gu.to_device(b_bits, w.dtype)
+    c = mha.gemm_splitk(ta, tb)
+    c2 = mha.gemm(ta, tb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([rng.integers(0, w.M, 12), [0, w.M - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(0, w.N, 12), [0, w.N - 1]]))
+    a = oracle.decode(a_bits[rows], w.dtype)
+    b = oracle.decode(b_bits[:, cols], w.dtype)
+    for out, how in ((c, "split-K"), (c2, "plain")):
+        cg = out[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].float().cpu().numpy()
+        _check(cg.astype(np.float64), a, b, w.dtype,
+               f"{name} {how}, splits {mha.mha_gemm_splitk_splits(w.M, w.N, w.K, 0)}")

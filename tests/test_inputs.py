@@ -109,6 +109,6 @@ def test_draw_gemm_and_workloads():
     np.testing.assert_array_equal(a, a2)
     np.testing.assert_array_equal(b, b2)
     assert not np.array_equal(mi.draw_gemm(5, 7, 9, "bf16", seed=4)[0], a)
-    assert len(mi.GEMM) == 15
-    for name, w in mi.GEMM.items():
+    assert len(mi.GEMM) == 15 and len(mi.GEMM_MEMBOUND) == 3
+    for name, w in list(mi.GEMM.items()) + list(mi.GEMM_MEMBOUND.items()):
         assert name == f"bf16_gemm_M{w.M}_N{w.N}_K{w.K}" and w.flops() == 2.0 * w.M * w.N * w.K
