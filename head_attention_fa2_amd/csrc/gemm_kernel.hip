@@ -10,7 +10,8 @@
 //    2 x 4 grid and each accumulates a 128 x 64 sub-block in 8 float32 accumulators of
 //    v_mfma_f32_32x32x16_{bf16,f16} (128 VGPRs).  One workgroup per CU (128 KiB of LDS).
 //    Grids of fewer than 192 such tiles use 128 x 128 blocks of 4 wavefronts (64 x 64
-//    each, two workgroups per CU) instead, so that they fill the 256 CUs.
+//    each, two workgroups per CU) instead, and grids of fewer than 384 of those 128 x 64
+//    blocks (64 x 32 per wavefront, three workgroups per CU), so that they fill the CUs.
 //  * The product is formed transposed per 32 x 32 block, C^T = B^T.A^T, so that after
 //    the MFMA every lane holds 8 consecutive columns of one row of C (16-byte stores).
 //    The B^T operand comes from row-major B in LDS through ds_read_b64_tr_b16, the
@@ -83,18 +84,23 @@ struct Tiling {
   static constexpr int ATile = BM * BK * 2, BTile = BK * BN * 2, Stage = ATile + BTile;
   static constexpr int LoadsA = ATile / 16 / Threads, LoadsB = BTile / 16 / Threads;
   static_assert(LoadsA * 16 * Threads == ATile && LoadsB * 16 * Threads == BTile, "even split");
-  static_assert(MB >= 1 && NB >= 1 && (RB == 16 || RB == 32), "supported shapes");
+  static_assert(MB >= 1 && NB >= 1 && (RB == 8 || RB == 16 || RB == 32), "supported shapes");
 };
 // 256 x 256, 8 wavefronts of 128 x 64, one workgroup per CU (128 KiB of LDS).
 typedef Tiling<256, 256, 2, 4> Large;
 // 128 x 128, 4 wavefronts of 64 x 64, two workgroups per CU (64 KiB of LDS each): four
 // times the tiles, for grids that would not fill the 256 CUs.
 typedef Tiling<128, 128, 2, 2> Small;
+// 128 x 64, 4 wavefronts of 64 x 32, three workgroups per CU (48 KiB of LDS each).
+typedef Tiling<128, 64, 2, 2> Tiny;
 constexpr int kGroupM = 8;                 // block-rows per group of the tile order
 // Below this many 256 x 256 tiles (3/4 of the 256 CUs) the 128 x 128 tiling is used.
 // Measured on the Llama-3-8B shapes: 64 and 128 tiles run 1.2-1.7x faster as 128 x 128,
 // 224 tiles and more 1.2-1.3x slower.
 constexpr long kLargeMinTiles = 192;
+// Below this many 128 x 128 tiles (1.5 per CU) the 128 x 64 tiling is used: measured
+// 1.15-1.2x faster at 48-256 tiles, 1.5x slower at 512.
+constexpr long kSmallMinTiles = 384;
 
 struct GemmParams {
   const void* a;
@@ -359,10 +365,12 @@ void launch_tiled(GemmParams p, int dtype, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_kernel<__bf16, C>), dim3(p.total), dim3(C::Threads), 0, stream, p);
 }
 
-// 1: the 128 x 128 tiling, 0: the 256 x 256 one.
+// 0: the 256 x 256 tiling, 1: 128 x 128, 2: 128 x 64.
 int gemm_tiling(int M, int N) {
-  const long tiles = (long)((M + Large::BM - 1) / Large::BM) * ((N + Large::BN - 1) / Large::BN);
-  return tiles < kLargeMinTiles ? 1 : 0;
+  const long large = (long)((M + Large::BM - 1) / Large::BM) * ((N + Large::BN - 1) / Large::BN);
+  if (large >= kLargeMinTiles) return 0;
+  const long small = (long)((M + Small::BM - 1) / Small::BM) * ((N + Small::BN - 1) / Small::BN);
+  return small >= kSmallMinTiles ? 1 : 2;
 }
 
 }  // namespace
@@ -376,10 +384,13 @@ hipError_t launch_gemm(const void* a, const void* b, void* c, int M, int N, int 
   p.M = M;
   p.N = N;
   p.K = K;
-  if (gemm_tiling(M, N) == 1)
+  const int tiling = gemm_tiling(M, N);
+  if (tiling == 0)
+    launch_tiled<Large>(p, dtype, stream);
+  else if (tiling == 1)
     launch_tiled<Small>(p, dtype, stream);
   else
-    launch_tiled<Large>(p, dtype, stream);
+    launch_tiled<Tiny>(p, dtype, stream);
   return hipGetLastError();
 }
 

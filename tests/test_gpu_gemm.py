@@ -2,8 +2,9 @@
 CPU oracle's float64 product, within the oracle's bound for a float32-accumulated,
 once-rounded result (u_out |C| + gamma_K |A||B|, bf16 u = 2^-8, fp16 u = 2^-11).  The
 element-wise shapes cover ragged M, N and K (partial tiles, K not a multiple of the
-64-wide k-step) under both tilings (128 x 128 below 192 tiles of 256 x 256, 256 x 256
-from there); the full-size workloads are checked on sampled rows and columns."""
+64-wide k-step) under the three tilings (256 x 256 from 192 such tiles, else 128 x 128
+from 384 such tiles, else 128 x 64); the full-size workloads are checked on sampled rows
+and columns."""
 import numpy as np
 import pytest
 import torch
@@ -40,6 +41,8 @@ CASES = [
     (2048, 256, 4104, "bf16"), (96, 64, 4096, "bf16"),
     # 208 tiles of 256 x 256: the large tiling, ragged in M, N and K
     (4000, 3080, 1000, "bf16"), (3900, 3336, 264, "f16"),
+    # 384-400 tiles of 128 x 128 (and under 192 large ones): the 128 x 128 tiling
+    (2048, 3072, 264, "bf16"), (2000, 3080, 136, "f16"),
 ]
 
 
