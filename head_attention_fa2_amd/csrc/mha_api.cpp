@@ -125,8 +125,10 @@ mha_status validate_gemm(const void* a, const void* b, const void* c, int M, int
   if (dtype == MHA_DTYPE_F32) return MHA_ERR_UNSUPPORTED;
   if (N % 8 != 0 || K % 8 != 0) return MHA_ERR_UNSUPPORTED;
   if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return MHA_ERR_UNSUPPORTED;
-  // 32-bit byte offsets inside A and B; the tile count fits the grid
+  // 32-bit byte offsets inside A and B; the tile count (at the smallest tiling, 128 x 64)
+  // fits the grid
   if ((int64_t)M * K * 2 > UINT32_MAX || (int64_t)K * N * 2 > UINT32_MAX) return MHA_ERR_UNSUPPORTED;
+  if (((int64_t)M + 127) / 128 * (((int64_t)N + 63) / 64) > INT32_MAX) return MHA_ERR_UNSUPPORTED;
   return MHA_OK;
 }
 

@@ -247,7 +247,8 @@ double mha_fwd_paged_bytes(int B, int H, int Nq, long long total_keys, int d, mh
  *
  * Errors: MHA_ERR_INVALID_ARG for a null pointer, a size < 1 or an unknown dtype;
  * MHA_ERR_UNSUPPORTED for fp32, N or K not a multiple of 8, a pointer not 16-byte
- * aligned, or an operand of 4 GiB or more; MHA_ERR_HIP if the launch fails.
+ * aligned, an operand of 4 GiB or more, or more than 2^31 - 1 blocks of 128 x 64;
+ * MHA_ERR_HIP if the launch fails.
  */
 mha_status mha_gemm(const void* a, const void* b, void* c, int M, int N, int K, mha_dtype dtype,
                     void* stream);

@@ -197,6 +197,7 @@ def test_paged_bytes():
     (dict(a=0), INVALID), (dict(c=0), INVALID), (dict(M=0), INVALID), (dict(K=-8), INVALID), (dict(dtype=7), INVALID),
     (dict(dtype=F32), UNSUPPORTED), (dict(N=12), UNSUPPORTED), (dict(K=100), UNSUPPORTED),
     (dict(b=P + 8), UNSUPPORTED), (dict(M=1 << 20, K=4096), UNSUPPORTED), (dict(N=1 << 19, K=8192), UNSUPPORTED),
+    (dict(M=(1 << 27) - 1, N=(1 << 27) - 8, K=8), UNSUPPORTED),
 ])
 def test_gemm_validate(kw, code):
     a = dict(a=P, b=P, c=P, M=1000, N=4096, K=4096, dtype=BF16)
