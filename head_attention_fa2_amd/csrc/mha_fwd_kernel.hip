@@ -85,7 +85,13 @@ struct Half16<_Float16> {
 };
 
 constexpr int kQW = 32;                  // query rows per wavefront
-constexpr int kBN = 64;                  // keys per K/V tile
+// Keys per K/V tile: 32 for the fused kernel on 16-bit inputs with d = 128 (a 32 KiB
+// double-buffered tile set and 162 VGPRs let three workgroups share a CU; measured +1-4 %
+// on d = 128 against 64-key tiles at two workgroups per CU, but -4 % at d = 64), 64
+// otherwise.
+template <typename T, int D, bool SPLIT>
+constexpr int tile_keys() { return sizeof(T) == 2 && D == 128 && !SPLIT ? 32 : 64; }
+constexpr int kBN = 64;                  // keys per K/V tile of the split-KV kernels
 constexpr int kWaves = 4;                // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kQW * kWaves;        // query rows per workgroup
@@ -156,9 +162,12 @@ using gfx950::wait_vmcnt;
 
 // ---------------------------------------------------------------------------- kernel
 // Two workgroups (8 wavefronts) per CU when the double-buffered K/V tiles fit twice in
-// the 160 KiB of LDS; fp32 with d = 128 needs 128 KiB and runs one workgroup per CU.
-template <typename T, int D>
-constexpr int min_waves_per_eu() { return 2 * 2 * kBN * D * (int)sizeof(T) <= 80 * 1024 ? 2 : 1; }
+// the 160 KiB of LDS (three with the 32-key tiles); fp32 with d = 128 needs 128 KiB and
+// runs one workgroup per CU.
+template <typename T, int D, bool SPLIT>
+constexpr int min_waves_per_eu() {
+  return tile_keys<T, D, SPLIT>() == 32 ? 3 : 2 * 2 * kBN * D * (int)sizeof(T) <= 80 * 1024 ? 2 : 1;
+}
 
 // SPLIT: the split-KV form (no mask): workgroup (split, head, query block) covers the
 // keys [split * chunk, min(Nk, (split + 1) * chunk)) and writes its O (normalised by its
@@ -166,10 +175,12 @@ constexpr int min_waves_per_eu() { return 2 * 2 * kBN * D * (int)sizeof(T) <= 80
 // PAGED (with SPLIT): K and V are gathered from block pools [num_blocks][H][bs][d]
 // through the block table; head b*H + h uses keys [0, seq_lens[b]).
 template <typename T, int D, bool CAUSAL, bool SPLIT = false, bool PAGED = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<T, D>())))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<T, D, SPLIT>())))
 void mha_fwd_kernel(Params p) {
   static_assert(!(SPLIT && CAUSAL), "the split-KV form has no mask");
   static_assert(!PAGED || SPLIT, "paged K/V uses the split-KV form");
+  constexpr int kBN = tile_keys<T, D, SPLIT>();  // keys per K/V tile
+  constexpr int kSlabs = kBN / 32;               // 32-key MFMA slabs per tile
   constexpr bool k16 = sizeof(T) == 2;         // bf16 or fp16 inputs
   typedef typename Half16<T>::v8 h8_t;
   constexpr int RB = D * (int)sizeof(T);        // bytes per K/V row
@@ -362,37 +373,38 @@ void mha_fwd_kernel(Params p) {
   const float c2 = p.scale2;
 
   auto compute_tile = [&](const char* lk, const char* lv, int k0, bool masked) __attribute__((always_inline)) {
-    // S^T = K_j . Q^T : two 32-key slabs, accumulated in alternation so consecutive
+    // S^T = K_j . Q^T : one or two 32-key slabs, accumulated in alternation so consecutive
     // MFMAs are independent; K operands are read two steps ahead.
-    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+    f32x16_t s[kSlabs] = {};
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (k16) {
       constexpr int KC = D / 16;
-      h8_t kf[KC][2];
+      h8_t kf[KC][kSlabs];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) kf[kc][ks] = *(const h8_t*)(lk + offK[kc] + ks * 32 * RB);
+        for (int ks = 0; ks < kSlabs; ++ks) kf[kc][ks] = *(const h8_t*)(lk + offK[kc] + ks * 32 * RB);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < kSlabs; ++ks)
           s[ks] = Half16<T>::mma(kf[kc][ks], qf[kc], s[ks]);
-      // schedule: 4 reads, then (2 MFMA, 2 reads) ..., then the last MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      // schedule: 2 steps of reads, then (one step of MFMAs, one of reads) ..., then the
+      // last MFMAs (a step: one per slab)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kSlabs, 0);
 #pragma unroll
       for (int i = 0; i < KC - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kSlabs, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kSlabs, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kSlabs, 0);
     } else {
 #pragma unroll
       for (int j = 0; j < D / 8; ++j)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < kSlabs; ++ks) {
           const f32x4_t kf = *(const f32x4_t*)(lk + offK[j] + ks * 32 * RB);
 #pragma unroll
           for (int t = 0; t < 4; ++t)
@@ -407,7 +419,7 @@ void mha_fwd_kernel(Params p) {
     if (masked) {
       const int lim = CAUSAL ? min(qrow, N - 1) : kend - 1;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < kSlabs; ++ks)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * ks + 16 * (r >> 3) + 8 * G + (r & 7);
@@ -417,7 +429,7 @@ void mha_fwd_kernel(Params p) {
     // Online softmax (running max / sum of the "Long Softmax" puzzle).
     float mx = s[0][0];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < kSlabs; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ks][r]);
     mx = max_halves(mx);
@@ -434,7 +446,7 @@ void mha_fwd_kernel(Params p) {
     const float mc = (m_run == -__builtin_inff() ? 0.f : m_run) * c2;
     float lsum = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < kSlabs; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = fast_exp2(__builtin_fmaf(s[ks][r], c2, -mc));
@@ -447,16 +459,16 @@ void mha_fwd_kernel(Params p) {
     __builtin_amdgcn_sched_barrier(0);
     // O^T += V_j^T . P^T
     if constexpr (k16) {
-      h8_t pf[4];   // P^T operand for key chunks kc2 = 2ks + hh (16 keys each)
+      h8_t pf[2 * kSlabs];   // P^T operand for key chunks kc2 = 2ks + hh (16 keys each)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < kSlabs; ++ks)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int e = 0; e < 8; ++e) pf[2 * ks + hh][e] = (T)s[ks][8 * hh + e];
-      h8_t vf[4][kDT];
+      h8_t vf[2 * kSlabs][kDT];
 #pragma unroll
-      for (int kc2 = 0; kc2 < 4; ++kc2)
+      for (int kc2 = 0; kc2 < 2 * kSlabs; ++kc2)
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
           const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -466,14 +478,14 @@ void mha_fwd_kernel(Params p) {
           vf[kc2][dt] = __builtin_bit_cast(h8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
-      for (int kc2 = 0; kc2 < 4; ++kc2)
+      for (int kc2 = 0; kc2 < 2 * kSlabs; ++kc2)
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt)
           acc[dt] = Half16<T>::mma(vf[kc2][dt], pf[kc2], acc[dt]);
       // schedule: 8 reads (4 operands), then (1 MFMA, 2 reads) ..., then the last MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int i = 0; i < 4 * kDT - 4; ++i) {
+      for (int i = 0; i < 2 * kSlabs * kDT - 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
@@ -484,7 +496,7 @@ void mha_fwd_kernel(Params p) {
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < kSlabs; ++ks)
 #pragma unroll
           for (int u = 0; u < 16; ++u) {
             const int key = 32 * ks + 16 * (u >> 3) + 8 * G + (u & 7);
