@@ -98,6 +98,7 @@ constexpr int kBM = kQW * kWaves;        // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;     // lazy-rescale threshold, in log2 units
+constexpr int kOrderHeads = 4;           // causal: heads per ordering group on an XCD
 
 struct Params {
   const void* q;
@@ -199,7 +200,7 @@ void mha_fwd_kernel(Params p) {
 
   // --- workgroup -> (head, query block).  Consecutive workgroup ids go to different
   // XCDs, so renumber: the k-th workgroup dispatched to XCD x gets task x*T/8 + k, which
-  // keeps every head's query blocks on one XCD.  Causal: latest (heaviest) blocks first.
+  // keeps every head's query blocks on one XCD (they share its L2).
   int id = blockIdx.x;
   if ((p.total & 7) == 0) id = (id & 7) * (p.total >> 3) + (id >> 3);
   int split = 0;
@@ -207,9 +208,28 @@ void mha_fwd_kernel(Params p) {
     split = id / (p.nqb * p.BH);
     id -= split * p.nqb * p.BH;
   }
-  const int bh = id / p.nqb;
-  int qb = id - bh * p.nqb;
-  if (CAUSAL) qb = p.nqb - 1 - qb;
+  int bh = id / p.nqb;
+  int qb = id - bh * p.nqb;          // dispatch rank within the head; causal: 0 = heaviest
+  if constexpr (CAUSAL) {
+    // Causal blocks differ in work (block qb sees (qb + 1) * kBM keys).  Taken head after
+    // head, the heaviest blocks of an XCD's last heads would start near the end and leave
+    // CUs idle in a long tail.  So when B*H is a multiple of 8 (each XCD owns whole heads
+    // [x*hx, (x+1)*hx)), an XCD runs its heads in groups of kOrderHeads, and inside a
+    // group the heaviest block of every head first, then the next heaviest, and so on.
+    // The blocks of one group's heads still run close together in time, so their K/V
+    // tiles are mostly read once into the XCD's L2.
+    const int BH = p.total / p.nqb;
+    if ((BH & 7) == 0) {
+      const int hx = BH >> 3, x = blockIdx.x & 7, k = blockIdx.x >> 3;
+      const int grp = k / (kOrderHeads * p.nqb);
+      const int r = k - grp * kOrderHeads * p.nqb;
+      const int gs = min(kOrderHeads, hx - grp * kOrderHeads);   // heads in this group
+      const int rank = r / gs;
+      bh = x * hx + grp * kOrderHeads + (r - rank * gs);
+      qb = rank;
+    }
+    qb = p.nqb - 1 - qb;
+  }
   const int N = p.N;                            // query rows
   int seq_b = 0, head_h = 0;                    // paged: sequence and head of this workgroup
   int Nk = SPLIT ? p.Nk : N;                    // keys

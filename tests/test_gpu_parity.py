@@ -183,6 +183,36 @@ def test_out_buffers_fully_overwritten():
     assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
 
 
+# Causal launches with B*H a multiple of 8 take the grouped dispatch order (each XCD owns
+# B*H/8 whole heads, run in groups of four, heaviest query blocks of a group first).
+# Element-wise against the oracle with 1, 2, 3, 5 and 9 heads per XCD (last group
+# partial for 3, 5 and 9) and ragged query blocks.
+GROUPED = [(1, 8, 300, 64, "bf16"), (2, 8, 260, 128, "bf16"), (3, 8, 200, 64, "f16"),
+           (5, 8, 257, 128, "bf16"), (1, 72, 130, 128, "f16")]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype", GROUPED)
+def test_causal_grouped_order_elementwise(B, H, N, d, dtype):
+    q, k, v = gu.draw(B, H, N, d, dtype, seed=2000 + B * H + N)
+    scale = 1 / math.sqrt(d)
+    o, lse = gu.run(q, k, v, dtype, True, scale)
+    o_ref, l_ref = gu.oracle_full(q, k, v, dtype, True, scale)
+    _check(o, lse, o_ref, l_ref, dtype, f"grouped causal B{B} H{H} N{N} d{d} {dtype}")
+
+
+@pytest.mark.parametrize("B,H,N,d", [(4, 32, 4096, 128), (1, 32, 16384, 128), (3, 40, 1000, 64)])
+def test_causal_every_row_written(B, H, N, d):
+    """Full-size causal launches: outputs pre-filled with NaN come back finite, so every
+    (head, query block) pair was taken by exactly one workgroup's dispatch slot."""
+    g = torch.Generator(device="cuda").manual_seed(B * H + N)
+    q, k, v = (torch.randn(B, H, N, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device=q.device)
+    mha.fwd(q, k, v, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+
+
 def test_errors_raise():
     q = torch.zeros(1, 1, 16, 96, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(mha.MhaError) as e:
