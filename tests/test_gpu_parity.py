@@ -188,7 +188,7 @@ def test_out_buffers_fully_overwritten():
 # Element-wise against the oracle with 1, 2, 3, 5 and 9 heads per XCD (last group
 # partial for 3, 5 and 9) and ragged query blocks.
 GROUPED = [(1, 8, 300, 64, "bf16"), (2, 8, 260, 128, "bf16"), (3, 8, 200, 64, "f16"),
-           (5, 8, 257, 128, "bf16"), (1, 72, 130, 128, "f16")]
+           (5, 8, 257, 128, "bf16"), (1, 72, 130, 128, "f16"), (1, 8, 100, 128, "bf16"), (2, 4, 1, 64, "f16")]
 
 
 @pytest.mark.parametrize("B,H,N,d,dtype", GROUPED)
