@@ -11,10 +11,11 @@
 // wavefront reads all of K/V, so wavefronts never exchange partial results.
 //
 // Mapping onto CDNA4:
-//  * A workgroup of 4 wavefronts owns 128 query rows, 32 per wavefront; two
-//    workgroups (8 wavefronts, 2 per SIMD) share a CU.  A wavefront raises its issue
-//    priority (s_setprio) while it feeds the matrix cores and drops it for the
-//    softmax, so the other wavefront of the SIMD fills the MFMA shadow with VALU work.
+//  * A workgroup of 4 wavefronts owns 128 query rows, 32 per wavefront; three
+//    workgroups (12 wavefronts, 3 per SIMD) share a CU at d = 128 on 16-bit inputs, up
+//    to four at d = 64.  A wavefront raises its issue priority (s_setprio) while it
+//    feeds the matrix cores with independent MFMAs and drops it for the softmax, so the
+//    other wavefronts of the SIMD fill the MFMA shadow with VALU work.
 //  * Both contractions are v_mfma_f32_32x32x16_bf16 (fp32 inputs: v_mfma_f32_32x32x2_f32).
 //    The scores are formed transposed, S^T = K.Q^T, so that the 32 lanes of a column
 //    each own ONE query row: row max / row sum are in-lane reductions plus one
@@ -24,7 +25,8 @@
 //    index inside each 32-row slab; the fp32 accumulator of S^T is then, register for
 //    register, the bf16 B operand P^T of the second product (8 consecutive keys per
 //    lane half), so P needs no cross-lane shuffle.
-//  * K/V tiles (64 keys) are copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+//  * K/V tiles (32 keys at d = 128 on 16-bit inputs, else 64) are copied HBM -> LDS
+//    with global_load_lds_dwordx4 (no VGPR
 //    staging), double buffered with one barrier per tile: after the barrier of step j
 //    every wavefront has finished step j-1, so tile j+1 is copied into that buffer and
 //    stays in flight while tile j is consumed.
@@ -38,8 +40,8 @@
 //    m + ln l are exact for whichever offset was used.
 //  * Causal: key tiles entirely above a wavefront's rows are skipped, only tiles that
 //    cross the diagonal (or the ragged end of the sequence) evaluate the mask, and
-//    heavy (late) query blocks are scheduled first.  Workgroup ids are remapped so that
-//    all query blocks of a head run on the same XCD and share its L2.
+//    heavy (late) query blocks are dispatched first.  Workgroup ids are
+//    remapped so that all query blocks of a head run on the same XCD and share its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -162,9 +164,11 @@ using gfx950::uniform_ptr;
 using gfx950::wait_vmcnt;
 
 // ---------------------------------------------------------------------------- kernel
-// Two workgroups (8 wavefronts) per CU when the double-buffered K/V tiles fit twice in
-// the 160 KiB of LDS (three with the 32-key tiles); fp32 with d = 128 needs 128 KiB and
-// runs one workgroup per CU.
+// Occupancy the register allocation must allow (wavefronts per SIMD = workgroups per
+// CU): three for the 32-key tiles (32 KiB of LDS, at most 168 VGPRs), two when the
+// double-buffered 64-key tiles fit twice in the 160 KiB of LDS, else one (fp32 with
+// d = 128 needs 128 KiB).  Kernels that need fewer registers may run more (d = 64 on
+// 16-bit inputs: four).
 template <typename T, int D, bool SPLIT>
 constexpr int min_waves_per_eu() {
   return tile_keys<T, D, SPLIT>() == 32 ? 3 : 2 * 2 * kBN * D * (int)sizeof(T) <= 80 * 1024 ? 2 : 1;
