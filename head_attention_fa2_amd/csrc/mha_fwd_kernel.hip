@@ -90,10 +90,9 @@ constexpr int kQW = 32;                  // query rows per wavefront
 // Keys per K/V tile: 32 for the fused kernel on 16-bit inputs with d = 128 (a 32 KiB
 // double-buffered tile set and 162 VGPRs let three workgroups share a CU; measured +1-4 %
 // on d = 128 against 64-key tiles at two workgroups per CU, but -4 % at d = 64), 64
-// otherwise.
+// otherwise (split-KV and paged kernels included).
 template <typename T, int D, bool SPLIT>
 constexpr int tile_keys() { return sizeof(T) == 2 && D == 128 && !SPLIT ? 32 : 64; }
-constexpr int kBN = 64;                  // keys per K/V tile of the split-KV kernels
 constexpr int kWaves = 4;                // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kQW * kWaves;        // query rows per workgroup
@@ -171,7 +170,8 @@ using gfx950::wait_vmcnt;
 // 16-bit inputs: four).
 template <typename T, int D, bool SPLIT>
 constexpr int min_waves_per_eu() {
-  return tile_keys<T, D, SPLIT>() == 32 ? 3 : 2 * 2 * kBN * D * (int)sizeof(T) <= 80 * 1024 ? 2 : 1;
+  constexpr int keys = tile_keys<T, D, SPLIT>();
+  return keys == 32 ? 3 : 2 * 2 * keys * D * (int)sizeof(T) <= 80 * 1024 ? 2 : 1;
 }
 
 // SPLIT: the split-KV form (no mask): workgroup (split, head, query block) covers the
