@@ -213,6 +213,27 @@ def test_causal_every_row_written(B, H, N, d):
     assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
 
 
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("bf16", 64, False), ("f16", 128, False),
+                                            ("f16", 64, True)])
+def test_long_sequence_sampled(dtype, d, causal):
+    """One head per batch entry with N = 65536 (2048 key tiles for the last query block):
+    sampled rows, including the first and last of several query blocks, against the oracle."""
+    B, H, N = 1, 2, 65536
+    q, k, v = gu.draw(B, H, N, d, dtype, seed=4000 + d + int(causal))
+    scale = 1 / math.sqrt(d)
+    tq, tk, tv = (gu.to_device(x, dtype) for x in (q, k, v))
+    o, lse = mha.fwd(tq, tk, tv, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rows = [0, 1, 127, 128, 4095, 32768, 65407, 65408, N - 1]
+    picks = [(0, h, r) for h in range(H) for r in rows]
+    o_ref, l_ref = oracle.attention_rows(q, k, v, causal=causal, scale=scale, picks=picks, dtype=dtype)
+    idx = torch.tensor(picks, dtype=torch.long, device=o.device)
+    og = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
+    lg = lse[idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy().astype(np.float64)
+    _check(og, lg, o_ref, l_ref, dtype, f"long N={N} d{d} causal={causal} {dtype}")
+
+
 def test_errors_raise():
     q = torch.zeros(1, 1, 16, 96, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(mha.MhaError) as e:
