@@ -174,8 +174,14 @@ def time_gemm(w, steps, warmup, dev, torch_too=True):
         torch.cuda.synchronize(dev)
         return ev[0].elapsed_time(ev[1]) / steps
 
-    ms = timed(lambda: mha.gemm(ta, tb, out=c, stream=stream))
-    ms_torch = timed(lambda: torch.matmul(ta, tb, out=c)) if torch_too else None
+    # three alternating passes, median of each, so that neither side times on colder clocks
+    ours, theirs = [], []
+    for _ in range(3):
+        ours.append(timed(lambda: mha.gemm(ta, tb, out=c, stream=stream)))
+        if torch_too:
+            theirs.append(timed(lambda: torch.matmul(ta, tb, out=c)))
+    ms = sorted(ours)[1]
+    ms_torch = sorted(theirs)[1] if torch_too else None
     mha.gemm(ta, tb, out=c, stream=stream)
     torch.cuda.synchronize(dev)
     return dict(ms=ms, ms_torch=ms_torch, inputs=(a, b), out=c)
@@ -414,7 +420,7 @@ def main():
             del rr
     if args.gemm:
         for name, ww in mha_inputs.GEMM.items():
-            rr = time_gemm(ww, max(10, args.steps // 4), 5, dev)
+            rr = time_gemm(ww, max(10, args.steps // 4), 20, dev)
             tf = ww.flops() / (rr["ms"] * 1e-3) / 1e12
             tft = ww.flops() / (rr["ms_torch"] * 1e-3) / 1e12
             print(json.dumps({"workload": name, "M": ww.M, "N": ww.N, "K": ww.K, "ms": round(rr["ms"], 5),
