@@ -13,9 +13,11 @@
 namespace mha_layout {
 
 // Chunk permutation inside a 256-byte LDS line, for lines holding one row (sw16) or two
-// rows (sw8).
+// rows (sw8).  sw8 puts line parity into bit 2: the transposing V^T read takes four
+// consecutive keys (two lines, one even and one odd) x four chunks in one pass, and the two
+// lines' chunks then fall into different halves of the bank groups.
 MHA_HD constexpr int sw16(int x) { return ((x >> 2) & 3) | ((x & 3) << 2); }
-MHA_HD constexpr int sw8(int x) { return ((x & 3) << 1) | ((x >> 2) & 1); }
+MHA_HD constexpr int sw8(int x) { return ((x & 1) << 2) | ((x >> 1) & 3); }
 
 // Byte offset in a K/V tile of 16-byte chunk c of row r, for rows of R chunks
 // (R = 8: 128-byte rows, two per line; R = 16: one 256-byte line; R = 32: two lines).

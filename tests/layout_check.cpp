@@ -5,8 +5,9 @@
 //  3. the K operand of every lane and step is row sigma(n) (+32 per slab), chunk 2kc+G;
 //  4. the V^T operand built by two ds_read_b64_tr_b16 per MFMA is, on lane L element e,
 //     V[16 kc2 + 8G + e][32 dt + sigma(L & 31)] (bf16 tiles);
-//  5. bank use: 16-lane groups of the K read and of each V^T read touch distinct
-//     16-byte bank groups (printed as a count of conflicting groups).
+//  5. bank use: each 16-lane pass of the K read (ds_read_b128) touches distinct 16-byte
+//     bank groups, and each 32-lane pass of a V^T read (ds_read_b64_tr_b16) asks no
+//     four-byte bank for two different words (printed as counts of conflicts).
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -87,11 +88,18 @@ void check(int elem_bytes) {
               CHECK(col == 32 * dt + sigma(L & 31), "R=%d V col L=%d e=%d", R, L, e);
             }
           }
-          for (int g = 0; g < 4; ++g) {
-            int used[16] = {0};
-            for (int l = 16 * g; l < 16 * g + 16; ++l)
-              used[((v_operand_off<R>(l, dt, h) + kc2 * 16 * RB) / 16) % 16]++;
-            for (int u : used) vconf += u > 2;   // each 16-byte group serves two 8-byte reads
+          // 32 lanes (256 bytes) per pass from 64 four-byte banks: a pass is free of
+          // conflicts when no bank is asked for two different words
+          for (int g = 0; g < 2; ++g) {
+            int word_of_bank[64];
+            for (int b = 0; b < 64; ++b) word_of_bank[b] = -1;
+            for (int l = 32 * g; l < 32 * g + 32; ++l)
+              for (int w = 0; w < 2; ++w) {
+                const int word = (v_operand_off<R>(l, dt, h) + kc2 * 16 * RB) / 4 + w;
+                int& slot = word_of_bank[word % 64];
+                if (slot >= 0 && slot != word) ++vconf;
+                slot = word;
+              }
           }
         }
   }
