@@ -112,6 +112,7 @@ int main() {
   check<16>(2);   // bf16 d=128
   check<16>(4);   // fp32 d=64
   check<32>(4);   // fp32 d=128
+  check<32>(2);   // 16-bit rows of 512 bytes: the GEMM's 256-column B tile, read as B^T
   printf(failures ? "layout check FAILED (%d)\n" : "layout check ok\n", failures);
   return failures ? 1 : 0;
 }
