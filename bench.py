@@ -40,19 +40,28 @@ def kernel_source_sha256() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per launch measured with rocprofv3 (FETCH_SIZE, WRITE_SIZE, each scaled
-    by the same counter's reading for a plain copy of known size), or None when no
-    measurement exists for the kernel source as it is now."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+def recorded_counters(workload: str) -> dict:
+    """Counter figures of the kernel on `workload` taken with rocprofv3 and stored in
+    profiles/kernel_counters.json, keyed by the SHA-256 of the kernel sources they were
+    taken on; a figure taken on other sources is reported as None.
+
+    traffic_bytes: HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, each scaled by the
+    same counter's reading for a plain copy of known size).
+    mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x CUs x GRBM_GUI_ACTIVE), the share of
+    the launch's cycles in which the matrix cores were busy.
+    hbm_gbs: traffic_bytes over the kernel-trace average duration."""
+    path = os.path.join(ROOT, "profiles", "kernel_counters.json")
+    out = {"traffic_bytes": None, "mfma_busy": None, "hbm_gbs": None}
     try:
         with open(path, encoding="utf-8") as fh:
             entry = json.load(fh).get(workload)
     except (OSError, ValueError):
-        return None
+        return out
     if not entry or entry.get("kernel_source_sha256") != kernel_source_sha256():
-        return None
-    return entry["traffic_bytes"]
+        return out
+    for key in out:
+        out[key] = entry.get(key)
+    return out
 
 
 def _to_device(a, dtype, dev):
@@ -65,8 +74,9 @@ def _to_device(a, dtype, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def time_gpu(w, steps, warmup, dev):
-    """Warm up, then time exactly `steps` launches bracketed by synchronisations."""
+def time_gpu(w, steps, warmup, dev, settle_s=0.0):
+    """Settle the clock, warm up, then time exactly `steps` launches bracketed by
+    synchronisations, with a HIP event on the launch stream between launches."""
     import torch
 
     import head_attention_fa2_amd as mha
@@ -77,20 +87,43 @@ def time_gpu(w, steps, warmup, dev):
     o = torch.empty_like(tq)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
+
+    def call():
         mha.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+
+    settle = settle_clock(call, dev, settle_s)
+    for _ in range(warmup):
+        call()
     torch.cuda.synchronize(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(steps):
-        mha.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        call()
         ev[i + 1].record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]      # ms, per launch
     total_ms = ev[0].elapsed_time(ev[steps])
-    return dict(total_ms=total_ms, per_ms=per, wall_s=wall, inputs=(q, k, v), out=(o, lse))
+    return dict(total_ms=total_ms, per_ms=per, wall_s=wall, settle=settle, inputs=(q, k, v), out=(o, lse))
+
+
+def settle_clock(call, dev, seconds):
+    """Launch `call` back to back until `seconds` of wall time have passed (at least one
+    launch), synchronising every few launches.  Under sustained load the MI355X lowers
+    its clock to its power limit within about a second; timing before that measures a
+    clock the workload does not keep.  Returns what ran: seconds and launches."""
+    import torch
+
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(8):
+            call()
+        n += 8
+        torch.cuda.synchronize(dev)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return {"settle_s": round(el, 3), "settle_launches": n}
 
 
 def time_gpu_splitkv(w, steps, warmup, dev):
@@ -288,9 +321,11 @@ def cpu_baseline(w, inputs, seconds):
     import oracle
 
     q, k, v = inputs
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    cores = host_workers()
     heads_per_call = max(1, min(w.H, math.ceil(cores / max(1, math.ceil(w.N / 1024)))))
     done_heads, t0 = 0, time.perf_counter()
+    outs = []
     with threadpool_limits(limits=1):
         while True:
             b, h0 = divmod(done_heads, w.H)
@@ -298,25 +333,56 @@ def cpu_baseline(w, inputs, seconds):
                 break
             h1 = min(w.H, h0 + heads_per_call)
             sl = (slice(b, b + 1), slice(h0, h1))
-            oracle.attention_forward(oracle.decode(q[sl], w.dtype), oracle.decode(k[sl], w.dtype),
-                                     oracle.decode(v[sl], w.dtype), causal=w.causal, scale=w.scale,
-                                     threads=cores)
+            outs.append((b, h0, h1) + oracle.attention_forward(
+                oracle.decode(q[sl], w.dtype), oracle.decode(k[sl], w.dtype), oracle.decode(v[sl], w.dtype),
+                causal=w.causal, scale=w.scale, threads=cores))
             done_heads += h1 - h0
             if time.perf_counter() - t0 >= seconds:
                 break
     el = time.perf_counter() - t0
     flops = w.credited_flops() / (w.B * w.H) * done_heads
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done_heads} of {w.B * w.H} heads (b, h in order) of {w.name}, float64, "
-                      f"{el:.1f} s wall, numpy/OpenBLAS 1 thread per worker x {cores} workers"}
+    res = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": f"{done_heads} of {w.B * w.H} heads (b, h in order) of {w.name}, float64, "
+                     f"{el:.1f} s wall, numpy/OpenBLAS 1 thread per worker x {cores} workers "
+                     f"({affinity} cores in the affinity mask)"}
+    return res, outs
+
+
+def host_workers() -> int:
+    """Worker threads for the host oracle: every core of the affinity mask, capped by the
+    CPU share the runtime grants this process (OMP_NUM_THREADS when set; one GPU's share
+    of a shared host is 16 cores)."""
+    n = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
+
+
+def parity_full(w, out, oracle_heads):
+    """Max abs error over every output element of the heads the CPU oracle evaluated."""
+    import numpy as np
+
+    o, lse = out
+    eo = el = 0.0
+    rows = 0
+    for b, h0, h1, o_ref, l_ref in oracle_heads:
+        og = o[b, h0:h1].float().cpu().numpy().astype(np.float64)
+        lg = lse[b, h0:h1].cpu().numpy().astype(np.float64)
+        eo = max(eo, float(np.max(np.abs(og - o_ref[0]))))
+        el = max(el, float(np.max(np.abs(lg - l_ref[0]))))
+        rows += (h1 - h0) * w.N
+    return {"rows": rows, "of_rows": w.B * w.H * w.N, "max_abs_dO": eo, "max_abs_dLSE": el}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU clock needs ~1 s of sustained work to settle; the default warm-up covers it
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=10)
+    # before the counted warm-up: launches for this many seconds, so that the clock has
+    # reached the level it holds under sustained load whatever --warmup is
+    ap.add_argument("--settle-seconds", type=float, default=1.5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -360,13 +426,15 @@ def main():
         return
     w = mha_inputs.WORKLOADS[args.workload]
 
-    r = time_gpu(w, args.steps, args.warmup, dev)
+    r = time_gpu(w, args.steps, args.warmup, dev, settle_s=args.settle_seconds)
     ms = r["total_ms"] / args.steps
     flops = w.credited_flops()
     tflops = flops / (ms * 1e-3) / 1e12
     avg_launch_ms = sum(r["per_ms"]) / len(r["per_ms"])
+    median_launch_ms = sorted(r["per_ms"])[len(r["per_ms"]) // 2]
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    ctr = recorded_counters(w.name)
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -382,17 +450,24 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "seed": w.seed, "pct_of_bf16_peak": round(100 * tflops / peak, 2)},
+        "settle": r["settle"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": recorded_traffic(w.name),
+                     "frac": round(achieved / peak, 4), "traffic": ctr["traffic_bytes"],
                      "kernel": f"mha_fwd_kernel<{w.dtype},{w.d},{'causal' if w.causal else 'full'}>",
                      "avg_launch_ms": round(avg_launch_ms, 5),
+                     "median_launch_ms": round(median_launch_ms, 5),
+                     "median_tflops": round(flops / (median_launch_ms * 1e-3) / 1e12, 2),
+                     "mfma_busy": ctr["mfma_busy"], "hbm_gbs": ctr["hbm_gbs"],
                      "algorithmic_bytes": mha.mha_fwd_bytes(w.B, w.H, w.N, w.d, 1 if w.dtype == "bf16" else 0)},
     }
-    if not args.no_parity:
-        line["parity"] = parity_sample(w, r["inputs"], r["out"])
+    oracle_heads = []
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, r["inputs"], args.cpu_seconds)
-    del r
+        line["cpu_baseline"], oracle_heads = cpu_baseline(w, r["inputs"], args.cpu_seconds)
+    if not args.no_parity:
+        # every element of the heads the CPU baseline evaluated, else sampled rows
+        line["parity"] = parity_full(w, r["out"], oracle_heads) if oracle_heads else \
+            parity_sample(w, r["inputs"], r["out"])
+    del r, oracle_heads
     if args.sweep:
         for name, ww in mha_inputs.WORKLOADS.items():
             rr = time_gpu(ww, max(5, args.steps // 2), 3, dev)

@@ -24,7 +24,7 @@ from typing import Optional, Tuple
 __all__ = [
     "MHA_OK", "MHA_ERR_INVALID_ARG", "MHA_ERR_UNSUPPORTED", "MHA_ERR_HIP",
     "MHA_DTYPE_F32", "MHA_DTYPE_BF16", "MHA_DTYPE_F16",
-    "library_path", "load", "mha_fwd", "mha_fwd_validate", "mha_fwd_flops",
+    "library_path", "serial_library_path", "load", "load_serial", "mha_fwd", "mha_fwd_validate", "mha_fwd_flops",
     "mha_fwd_bytes", "mha_fwd_splitkv", "mha_fwd_splitkv_validate", "mha_fwd_splitkv_splits",
     "mha_fwd_splitkv_workspace_size", "mha_fwd_splitkv_bytes", "mha_fwd_paged", "mha_fwd_paged_validate",
     "mha_fwd_paged_splits", "mha_fwd_paged_workspace_size", "mha_fwd_paged_bytes", "mha_status_string",
@@ -38,6 +38,7 @@ MHA_DTYPE_F32, MHA_DTYPE_BF16, MHA_DTYPE_F16 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB: Optional[ctypes.CDLL] = None
+_LIB_SERIAL: Optional[ctypes.CDLL] = None
 
 
 class MhaError(RuntimeError):
@@ -52,12 +53,29 @@ def library_path() -> str:
     return os.path.join(_HERE, "libmha.so")
 
 
+def serial_library_path() -> str:
+    return os.path.join(_HERE, "libmha_serial.so")
+
+
 def load() -> ctypes.CDLL:
     """Load libmha.so (built in place by ``head_attention_fa2_amd.build``)."""
     global _LIB
-    if _LIB is not None:
-        return _LIB
-    path = library_path()
+    if _LIB is None:
+        _LIB = _open(library_path())
+    return _LIB
+
+
+def load_serial() -> ctypes.CDLL:
+    """Load libmha_serial.so: the same C ABI built with MHA_SERIALIZE=1 (the race-check
+    form of the LDS tile loops, whose results must equal libmha.so's bit for bit).  For
+    tests; the functions of this module always call libmha.so."""
+    global _LIB_SERIAL
+    if _LIB_SERIAL is None:
+        _LIB_SERIAL = _open(serial_library_path())
+    return _LIB_SERIAL
+
+
+def _open(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with head_attention_fa2_amd.build.build()")
     lib = ctypes.CDLL(path)
@@ -111,7 +129,6 @@ def load() -> ctypes.CDLL:
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_version.argtypes = []
     lib.mha_version.restype = ctypes.c_char_p
-    _LIB = lib
     return lib
 
 

@@ -33,6 +33,13 @@
 #include <stdint.h>
 
 #include "gfx950_lds.h"
+
+// MHA_SERIALIZE=1: the race-check form of the k-step loop (one LDS buffer, each k-step
+// copied, waited for and fenced by barriers before and after it is read); same
+// arithmetic in the same order, so results equal the pipelined kernel's bit for bit.
+#ifndef MHA_SERIALIZE
+#define MHA_SERIALIZE 0
+#endif
 #include "mha_launch.h"
 #include "mha_layout.h"
 
@@ -259,7 +266,15 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
   };
 
   auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
+#if MHA_SERIALIZE
+    // race-check form: one buffer, copied, waited for and fenced before it is read
+    constexpr int buf = 0;
+    (void)buf_tag;
+    tile_barrier();
+    issue(t, 0, kA | kB);
+#else
     constexpr int buf = decltype(buf_tag)::value;
+#endif
     char* sa = smem + buf * kStage;
     wait_vmcnt<0>();
     const int k0 = kbeg + t * kBK;
@@ -270,6 +285,9 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
         if (k0 + a_k[j] >= K) *(uint4*)(sa + (j * kWaves + wave) * 1024 + lane * 16) = uint4{0, 0, 0, 0};
     }
     tile_barrier();
+#if MHA_SERIALIZE
+    compute(sa, sa + kATile, 0, kBK / 16);
+#else
     // the next step's copies go out between the first MFMAs of this one (measured: up
     // to a quarter faster than issuing them all before the first MFMA)
     compute(sa, sa + kATile, 0, 1);
@@ -277,9 +295,12 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
     compute(sa, sa + kATile, 1, 2);
     if (t + 1 < nk) issue(t + 1, buf ^ 1, kB);
     compute(sa, sa + kATile, 2, kBK / 16);
+#endif
   };
 
+#if !MHA_SERIALIZE
   issue(0, 0, kA | kB);
+#endif
   for (int t = 0; t < nk; t += 2) {
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < nk) step(t + 1, std::integral_constant<int, 1>{});

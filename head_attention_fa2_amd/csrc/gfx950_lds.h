@@ -19,8 +19,11 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 // sbase + voff and the data lands at LDS address lds + 16*l.  Issued as inline asm so
 // that the compiler does not track it: the only waits on these copies are the explicit
 // vmcnt waits of the tile pipeline, which order them against the LDS reads.
+// A load with LDS=1 reads m0 and needs one wait state after an SALU write of m0 (CDNA
+// ISA, manually inserted wait states); the compiler cannot see inside the asm block, so
+// the s_nop is written here.
 __device__ __forceinline__ void copy_to_lds(const void* sbase, unsigned voff, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds)
                : "memory", "m0");
@@ -28,7 +31,7 @@ __device__ __forceinline__ void copy_to_lds(const void* sbase, unsigned voff, un
 
 // As copy_to_lds, with a full 64-bit source address per lane (gathers from a block pool).
 __device__ __forceinline__ void copy_to_lds_addr(const void* src, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(src), "s"(lds)
                : "memory", "m0");

@@ -183,11 +183,11 @@ mha_status mha_fwd_validate(const void* q, const void* k, const void* v, const v
 }
 
 mha_status mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                   int N, int d, int causal, float scale, mha_dtype dtype, void* stream) {
+                   int N, int d, int causal, float scale, mha_dtype dtype, hipStream_t stream) {
   const mha_status st = validate(q, k, v, o, lse, B, H, N, d, causal, scale, dtype);
   if (st != MHA_OK) return st;
   const hipError_t e = mha_impl::launch_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, (int)dtype,
-                                            static_cast<hipStream_t>(stream));
+                                            stream);
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }
 
@@ -210,7 +210,7 @@ mha_status mha_fwd_splitkv_validate(const void* q, const void* k, const void* v,
 
 mha_status mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                            int Nq, int Nk, int d, float scale, mha_dtype dtype, int splits, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           size_t workspace_bytes, hipStream_t stream) {
   const mha_status st =
       validate_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits, workspace, workspace_bytes);
   if (st != MHA_OK) return st;
@@ -218,7 +218,7 @@ mha_status mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = part_o + (size_t)pt.splits * B * H * Nq * d;
   const hipError_t e = mha_impl::launch_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, (int)dtype, pt.splits,
-                                                    pt.chunk, part_o, part_lse, static_cast<hipStream_t>(stream));
+                                                    pt.chunk, part_o, part_lse, stream);
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }
 
@@ -234,7 +234,7 @@ mha_status mha_fwd_paged_validate(const void* q, const void* k_pool, const void*
 mha_status mha_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
                          const int32_t* seq_lens, void* o, float* lse, int B, int H, int Nq, int d, int num_blocks,
                          int block_size, int max_blocks, float scale, mha_dtype dtype, int splits, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, hipStream_t stream) {
   const mha_status st = validate_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H, Nq, d, num_blocks,
                                        block_size, max_blocks, scale, dtype, splits, workspace, workspace_bytes);
   if (st != MHA_OK) return st;
@@ -244,7 +244,7 @@ mha_status mha_fwd_paged(const void* q, const void* k_pool, const void* v_pool, 
   const hipError_t e = mha_impl::launch_fwd_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, B, H, Nq, d,
                                                   scale, (int)dtype, num_blocks, block_size_log2(block_size),
                                                   max_blocks, pt.splits, pt.chunk, part_o, part_lse,
-                                                  static_cast<hipStream_t>(stream));
+                                                  stream);
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }
 
@@ -269,10 +269,10 @@ mha_status mha_gemm_validate(const void* a, const void* b, const void* c, int M,
   return validate_gemm(a, b, c, M, N, K, dtype);
 }
 
-mha_status mha_gemm(const void* a, const void* b, void* c, int M, int N, int K, mha_dtype dtype, void* stream) {
+mha_status mha_gemm(const void* a, const void* b, void* c, int M, int N, int K, mha_dtype dtype, hipStream_t stream) {
   const mha_status st = validate_gemm(a, b, c, M, N, K, dtype);
   if (st != MHA_OK) return st;
-  const hipError_t e = mha_impl::launch_gemm(a, b, c, M, N, K, (int)dtype, static_cast<hipStream_t>(stream));
+  const hipError_t e = mha_impl::launch_gemm(a, b, c, M, N, K, (int)dtype, stream);
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }
 
@@ -292,12 +292,12 @@ mha_status mha_gemm_splitk_validate(const void* a, const void* b, const void* c,
 }
 
 mha_status mha_gemm_splitk(const void* a, const void* b, void* c, int M, int N, int K, mha_dtype dtype, int splits,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const mha_status st = validate_gemm_splitk(a, b, c, M, N, K, dtype, splits, workspace, workspace_bytes);
   if (st != MHA_OK) return st;
   const Partition pt = gemm_splitk_partition(M, N, K, splits);
   const hipError_t e = mha_impl::launch_gemm_splitk(a, b, c, M, N, K, (int)dtype, pt.splits, pt.chunk,
-                                                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+                                                    static_cast<float*>(workspace), stream);
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }
 

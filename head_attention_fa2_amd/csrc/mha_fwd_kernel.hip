@@ -55,6 +55,15 @@
 // reads m0, so declaring it clobbered is sound.
 #pragma clang diagnostic ignored "-Winline-asm"
 
+// MHA_SERIALIZE=1 builds the race-check form of the tile loop: one LDS buffer, and every
+// tile is copied, waited for and fenced by a barrier before any wavefront reads it, with a
+// second barrier before the next copy overwrites it.  No copy is ever in flight while
+// operands are read, and the arithmetic (and its order) is unchanged, so its results must
+// equal the pipelined kernel's bit for bit.
+#ifndef MHA_SERIALIZE
+#define MHA_SERIALIZE 0
+#endif
+
 namespace mha_impl {
 namespace {
 
@@ -540,6 +549,15 @@ void mha_fwd_kernel(Params p) {
   // --- main loop over K/V tiles, double buffered, one barrier per tile.  Unrolled by
   // two so that the LDS buffer of each step is a compile-time address.
   auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
+#if MHA_SERIALIZE
+    constexpr int buf = 0;
+    (void)buf_tag;
+    tile_barrier();                                    // every wavefront is done with tile t-1
+    if constexpr (PAGED) fetch_entries(t);
+    issue_tile(t, 0);
+    wait_vmcnt<0>();
+    tile_barrier();                                    // tile t has landed for every wavefront
+#else
     constexpr int buf = decltype(buf_tag)::value;
     wait_vmcnt<0>();
     tile_barrier();
@@ -547,6 +565,7 @@ void mha_fwd_kernel(Params p) {
     if constexpr (PAGED) {
       if (t + 2 < ntiles) fetch_entries(t + 2);
     }
+#endif
     const int k0 = kbeg + t * kBN;
     if (SPLIT && qw >= N) return;                      // no query row in this wavefront
     if (!CAUSAL || k0 <= qw + kQW - 1) {               // else: every key is after every row
@@ -554,11 +573,13 @@ void mha_fwd_kernel(Params p) {
       compute_tile(smem + buf * 2 * kTileBytes, smem + buf * 2 * kTileBytes + kTileBytes, k0, need_mask);
     }
   };
+#if !MHA_SERIALIZE
   if constexpr (PAGED) fetch_entries(0);
   issue_tile(0, 0);
   if constexpr (PAGED) {
     if (ntiles > 1) fetch_entries(1);
   }
+#endif
   for (int t = 0; t < ntiles; t += 2) {
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});

@@ -33,6 +33,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* hipStream_t as the HIP runtime defines it (a pointer to the opaque ihipStream_t), so
+ * that this header needs no HIP include: a caller that includes hip_runtime_api.h gets
+ * the same type, and any caller may pass NULL or a stream handle from another binding
+ * (for instance torch.cuda.current_stream().cuda_stream). */
+#if !defined(HIP_INCLUDE_HIP_HIP_RUNTIME_API_H)
+typedef struct ihipStream_t* hipStream_t;
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -76,7 +84,7 @@ typedef enum mha_dtype {
  */
 mha_status mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int N, int d, int causal, float scale,
-                   mha_dtype dtype, void* stream);
+                   mha_dtype dtype, hipStream_t stream);
 
 /*
  * mha_fwd_validate -- the argument checks of mha_fwd alone, on the host, with no HIP
@@ -129,7 +137,7 @@ double mha_fwd_bytes(int B, int H, int N, int d, mha_dtype dtype);
  */
 mha_status mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Nq, int Nk, int d, float scale, mha_dtype dtype,
-                           int splits, void* workspace, size_t workspace_bytes, void* stream);
+                           int splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* mha_fwd_splitkv_validate -- the argument checks of mha_fwd_splitkv alone, host only. */
 mha_status mha_fwd_splitkv_validate(const void* q, const void* k, const void* v, const void* o,
@@ -197,7 +205,7 @@ mha_status mha_fwd_paged(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
                          int B, int H, int Nq, int d, int num_blocks, int block_size,
                          int max_blocks, float scale, mha_dtype dtype, int splits,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * mha_fwd_paged_splits -- the number of key ranges mha_fwd_paged will use for a request
@@ -251,7 +259,7 @@ double mha_fwd_paged_bytes(int B, int H, int Nq, long long total_keys, int d, mh
  * MHA_ERR_HIP if the launch fails.
  */
 mha_status mha_gemm(const void* a, const void* b, void* c, int M, int N, int K, mha_dtype dtype,
-                    void* stream);
+                    hipStream_t stream);
 
 /* mha_gemm_validate -- the argument checks of mha_gemm alone, host only. */
 mha_status mha_gemm_validate(const void* a, const void* b, const void* c, int M, int N, int K,
@@ -279,7 +287,7 @@ mha_status mha_gemm_validate(const void* a, const void* b, const void* c, int M,
  * Two kernels are enqueued on `stream`.
  */
 mha_status mha_gemm_splitk(const void* a, const void* b, void* c, int M, int N, int K, mha_dtype dtype,
-                           int splits, void* workspace, size_t workspace_bytes, void* stream);
+                           int splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* mha_gemm_splitk_validate -- the argument checks of mha_gemm_splitk alone, host only. */
 mha_status mha_gemm_splitk_validate(const void* a, const void* b, const void* c, int M, int N, int K,

@@ -1,6 +1,9 @@
 """Helpers for GPU tests: move seeded inputs to the device and outputs back."""
+import os
+
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
 import head_attention_fa2_amd as mha
 import mha_inputs
@@ -26,9 +29,22 @@ def run(q, k, v, dtype, causal, scale=None, stream=None):
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def oracle_full(q, k, v, dtype, causal, scale):
-    return oracle.attention_forward(oracle.decode(q, dtype), oracle.decode(k, dtype),
-                                    oracle.decode(v, dtype), causal=causal, scale=scale)
+def host_threads() -> int:
+    """Threads for the host oracle: the affinity mask, capped by the CPU share the
+    runtime grants (OMP_NUM_THREADS when set)."""
+    n = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(share)) if share.isdigit() and int(share) > 0 else n)
+
+
+def oracle_full(q, k, v, dtype, causal, scale, threads=1):
+    """The float64 oracle over whole tensors; with threads > 1 the (batch, head, row-chunk)
+    items run on a thread pool with one BLAS thread each."""
+    args = (oracle.decode(q, dtype), oracle.decode(k, dtype), oracle.decode(v, dtype))
+    if threads <= 1:
+        return oracle.attention_forward(*args, causal=causal, scale=scale)
+    with threadpool_limits(limits=1):
+        return oracle.attention_forward(*args, causal=causal, scale=scale, threads=threads)
 
 
 def draw(B, H, N, d, dtype, seed, qk_sigma=1.0, v_uniform=False):
