@@ -22,7 +22,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "MHA_OK", "MHA_ERR_INVALID_ARG", "MHA_ERR_UNSUPPORTED", "MHA_ERR_HIP",
+    "MHA_OK", "MHA_ERR_INVALID_ARG", "MHA_ERR_UNSUPPORTED", "MHA_ERR_HIP", "MHA_ERR_SCRATCH",
+    "MHA_SCRATCH_BYTES", "mha_fwd_splitkv_noalloc",
     "MHA_DTYPE_F32", "MHA_DTYPE_BF16", "MHA_DTYPE_F16",
     "library_path", "serial_library_path", "load", "load_serial", "mha_fwd", "mha_fwd_validate", "mha_fwd_flops",
     "mha_fwd_bytes", "mha_fwd_splitkv", "mha_fwd_splitkv_validate", "mha_fwd_splitkv_splits",
@@ -33,7 +34,8 @@ __all__ = [
     "fwd", "fwd_splitkv", "fwd_paged", "gemm", "gemm_splitk", "MhaError",
 ]
 
-MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_HIP = 0, 1, 2, 3
+MHA_OK, MHA_ERR_INVALID_ARG, MHA_ERR_UNSUPPORTED, MHA_ERR_HIP, MHA_ERR_SCRATCH = 0, 1, 2, 3, 4
+MHA_SCRATCH_BYTES = 16 << 20    # the static scratch of mha_fwd_splitkv_noalloc (include/mha.h)
 MHA_DTYPE_F32, MHA_DTYPE_BF16, MHA_DTYPE_F16 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +93,8 @@ def _open(path: str) -> ctypes.CDLL:
     sz = ctypes.c_size_t
     lib.mha_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.mha_fwd_splitkv.restype = i
+    lib.mha_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.mha_fwd_splitkv_noalloc.restype = i
     lib.mha_fwd_splitkv_validate.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz]
     lib.mha_fwd_splitkv_validate.restype = i
     lib.mha_fwd_splitkv_splits.argtypes = [i, i, i, i, i]
@@ -158,6 +162,13 @@ def mha_fwd_splitkv(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq
     """Enqueue the split-KV forward (partials, then the merge) on ``stream``."""
     return load().mha_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits,
                                   workspace, workspace_bytes, stream)
+
+
+def mha_fwd_splitkv_noalloc(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int,
+                            d: int, scale: float, dtype: int, splits: int, stream: int) -> int:
+    """mha_fwd_splitkv with the partial results in the library's static device scratch
+    (no workspace, no allocation); pointers are device addresses (ints)."""
+    return load().mha_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits, stream)
 
 
 def mha_fwd_splitkv_validate(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int,

@@ -64,22 +64,31 @@ size_t workspace_bytes(int B, int H, int Nq, int d, int splits) {
   return (size_t)splits * (size_t)B * (size_t)H * (size_t)Nq * ((size_t)d + 1) * sizeof(float);
 }
 
-mha_status validate_splitkv(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                            int B, int H, int Nq, int Nk, int d, float scale, mha_dtype dtype, int splits,
-                            const void* workspace, size_t ws_bytes) {
-  if (!q || !k || !v || !o || !lse || !workspace) return MHA_ERR_INVALID_ARG;
+// Split-KV checks of everything but the workspace.
+mha_status validate_splitkv_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                 int B, int H, int Nq, int Nk, int d, float scale, mha_dtype dtype, int splits) {
+  if (!q || !k || !v || !o || !lse) return MHA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || splits < 0) return MHA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return MHA_ERR_INVALID_ARG;
   if (dtype != MHA_DTYPE_F32 && dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_F16) return MHA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return MHA_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(workspace))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return MHA_ERR_UNSUPPORTED;
   const Partition pt = partition(B, H, Nq, Nk, splits);
-  if (ws_bytes < workspace_bytes(B, H, Nq, d, pt.splits)) return MHA_ERR_INVALID_ARG;
   const int64_t bm = mha_impl::fwd_query_block((int)dtype);
   const int64_t blocks = ((int64_t)Nq + bm - 1) / bm * (int64_t)B * (int64_t)H * pt.splits;
   if (blocks > INT32_MAX || (int64_t)B * H * Nq > INT32_MAX) return MHA_ERR_UNSUPPORTED;
+  return MHA_OK;
+}
+
+mha_status validate_splitkv(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                            int B, int H, int Nq, int Nk, int d, float scale, mha_dtype dtype, int splits,
+                            const void* workspace, size_t ws_bytes) {
+  if (!workspace) return MHA_ERR_INVALID_ARG;
+  const mha_status st = validate_splitkv_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits);
+  if (st != MHA_OK) return st;
+  if (!aligned16(workspace)) return MHA_ERR_UNSUPPORTED;
+  if (ws_bytes < workspace_bytes(B, H, Nq, d, partition(B, H, Nq, Nk, splits).splits)) return MHA_ERR_INVALID_ARG;
   return MHA_OK;
 }
 
@@ -222,6 +231,22 @@ mha_status mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }
 
+mha_status mha_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                   int Nq, int Nk, int d, float scale, mha_dtype dtype, int splits,
+                                   hipStream_t stream) {
+  const mha_status st = validate_splitkv_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits);
+  if (st != MHA_OK) return st;
+  const Partition pt = partition(B, H, Nq, Nk, splits);
+  if (workspace_bytes(B, H, Nq, d, pt.splits) > mha_impl::scratch_bytes()) return MHA_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (mha_impl::scratch_address(&scratch) != hipSuccess) return MHA_ERR_HIP;
+  float* part_o = static_cast<float*>(scratch);
+  float* part_lse = part_o + (size_t)pt.splits * B * H * Nq * d;
+  const hipError_t e = mha_impl::launch_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, (int)dtype, pt.splits,
+                                                    pt.chunk, part_o, part_lse, stream);
+  return e == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
 mha_status mha_fwd_paged_validate(const void* q, const void* k_pool, const void* v_pool,
                                   const int32_t* block_table, const int32_t* seq_lens, const void* o,
                                   const float* lse, int B, int H, int Nq, int d, int num_blocks, int block_size,
@@ -329,6 +354,7 @@ const char* mha_status_string(mha_status status) {
     case MHA_ERR_INVALID_ARG: return "MHA_ERR_INVALID_ARG: invalid argument";
     case MHA_ERR_UNSUPPORTED: return "MHA_ERR_UNSUPPORTED: unsupported head dim, alignment or size";
     case MHA_ERR_HIP: return "MHA_ERR_HIP: the HIP runtime rejected the launch";
+    case MHA_ERR_SCRATCH: return "MHA_ERR_SCRATCH: the call needs more than the library's static scratch";
   }
   return "unknown mha_status";
 }

@@ -45,6 +45,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "gfx950_lds.h"
@@ -721,6 +722,36 @@ hipError_t launch_split(const Params& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Static scratch of the no-allocation split-KV entry point: the float32 partial results
+// (O then LSE of every split) of a call, in place of a caller workspace.  Each GPU holds
+// its own copy at its own address; host code must use that address, never the array's
+// name (which on the host only stands for the symbol).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+size_t scratch_bytes() { return kScratchBytes; }
+
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 int fwd_query_block(int) { return kBM; }
 

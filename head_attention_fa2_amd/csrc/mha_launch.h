@@ -21,6 +21,11 @@ hipError_t launch_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               int Nq, int Nk, int d, float scale, int dtype, int splits, int chunk,
                               float* part_o, float* part_lse, hipStream_t stream);
 
+// The static device scratch of the no-allocation split-KV entry point: its address on
+// the current device (looked up once per device with hipGetSymbolAddress) and its size.
+hipError_t scratch_address(void** out);
+size_t scratch_bytes();
+
 // Enqueue the paged split-KV forward: as launch_fwd_splitkv, with K and V gathered from
 // block pools [num_blocks][H][2^bs_log2][d] through block_table [B][max_blocks]; sequence
 // b uses keys [0, seq_lens[b]) (clamped to [0, max_blocks << bs_log2]).  part_o /

@@ -51,7 +51,9 @@ typedef enum mha_status {
                               unknown dtype */
   MHA_ERR_UNSUPPORTED = 2, /* head dim not 64 or 128, pointer not 16-byte aligned,
                               grid larger than the launch limit */
-  MHA_ERR_HIP = 3          /* the HIP runtime rejected the launch */
+  MHA_ERR_HIP = 3,         /* the HIP runtime rejected the launch */
+  MHA_ERR_SCRATCH = 4      /* mha_fwd_splitkv_noalloc: the call needs more than the
+                              library's static scratch (MHA_SCRATCH_BYTES) */
 } mha_status;
 
 typedef enum mha_dtype {
@@ -138,6 +140,30 @@ double mha_fwd_bytes(int B, int H, int N, int d, mha_dtype dtype);
 mha_status mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Nq, int Nk, int d, float scale, mha_dtype dtype,
                            int splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mha_fwd_splitkv_noalloc -- mha_fwd_splitkv for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the float32 partial results go to a static device buffer of the library
+ * (MHA_SCRATCH_BYTES bytes on every GPU it runs on, held until the process ends) instead
+ * of a caller workspace.  The call allocates nothing; the caller passes q, k, v, o and
+ * lse as for mha_fwd_splitkv, and the results are those of mha_fwd_splitkv with the same
+ * arguments.
+ *
+ * The buffer's address on the current device is looked up on the first call made with
+ * that device current.  Every call on one GPU shares that GPU's buffer: calls that
+ * overlap in time on one GPU (different streams, host threads) race and must be ordered
+ * by the caller.  Nothing in the buffer needs clearing: each call writes every partial
+ * it reads.
+ *
+ * Errors as for mha_fwd_splitkv (without the workspace checks), plus MHA_ERR_SCRATCH when
+ * mha_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, splits) exceeds MHA_SCRATCH_BYTES, and
+ * MHA_ERR_HIP if the buffer's address cannot be obtained.
+ */
+#define MHA_SCRATCH_BYTES ((size_t)16 << 20)
+mha_status mha_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int B, int H, int Nq, int Nk, int d, float scale, mha_dtype dtype,
+                                   int splits, hipStream_t stream);
 
 /* mha_fwd_splitkv_validate -- the argument checks of mha_fwd_splitkv alone, host only. */
 mha_status mha_fwd_splitkv_validate(const void* q, const void* k, const void* v, const void* o,

@@ -39,6 +39,14 @@ void touch_partials(float* part_o, float* part_lse, int B, int H, int Nq, int d,
 namespace mha_impl {
 int fwd_query_block(int) { return 128; }
 
+// host stand-in for the static device scratch of mha_fwd_splitkv_noalloc: exactly its size
+size_t scratch_bytes() { return MHA_SCRATCH_BYTES; }
+hipError_t scratch_address(void** out) {
+  static std::vector<char> host_scratch(MHA_SCRATCH_BYTES);
+  *out = host_scratch.data();
+  return hipSuccess;
+}
+
 hipError_t launch_fwd(const void*, const void*, const void*, void*, float*, int B, int H, int N, int d,
                       int causal, float scale, int dtype, hipStream_t) {
   ++g_launches;
@@ -136,6 +144,27 @@ int main() {
                                            aligned, ws - 1) == MHA_ERR_INVALID_ARG);
             (void)mha_fwd_splitkv_bytes(B, H, Nq, Nk, d, MHA_DTYPE_BF16);
           }
+  // no-allocation form: the stub writes the partials into a host buffer of exactly
+  // MHA_SCRATCH_BYTES, so accepting a call that needs more would be a heap overflow
+  int noalloc_ok = 0, noalloc_rejected = 0;
+  for (int B : {1, 4, 64, 1000})
+    for (int Nq : {1, 16, 300})
+      for (int Nk : {1, 4096, 131072, 1 << 22})
+        for (int d : {64, 128})
+          for (int splits : {0, 1, 64, 4096}) {
+            const int H = 8;
+            const size_t need = mha_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, splits);
+            const mha_status r =
+                mha_fwd_splitkv_noalloc(p, p, p, w, lse, B, H, Nq, Nk, d, 0.1f, MHA_DTYPE_BF16, splits, nullptr);
+            CHECK(r == (need <= MHA_SCRATCH_BYTES ? MHA_OK : MHA_ERR_SCRATCH));
+            (r == MHA_OK ? noalloc_ok : noalloc_rejected)++;
+          }
+  CHECK(noalloc_ok > 0 && noalloc_rejected > 0);
+  CHECK(mha_fwd_splitkv_noalloc(nullptr, p, p, w, lse, 1, 1, 1, 8, 64, 1.f, MHA_DTYPE_BF16, 0, nullptr) ==
+        MHA_ERR_INVALID_ARG);
+  CHECK(mha_fwd_splitkv_noalloc(p, p, p, w, lse, 1, 1, 1, 8, 96, 1.f, MHA_DTYPE_BF16, 0, nullptr) ==
+        MHA_ERR_UNSUPPORTED);
+
   for (int a : ints)
     for (int b : ints) {
       (void)mha_fwd_splitkv_splits(a, 2, b, a, b);
@@ -192,7 +221,7 @@ int main() {
                 MHA_ERR_INVALID_ARG);
         }
 
-  for (int st = -1; st < 5; ++st) CHECK(mha_status_string((mha_status)st) != nullptr);
+  for (int st = -1; st < 6; ++st) CHECK(mha_status_string((mha_status)st) != nullptr);
   CHECK(std::strlen(mha_version()) > 0);
   std::printf("launches %d, failures %d\n", g_launches, g_failures);
   if (g_failures == 0) std::printf("abi sanitize ok\n");
