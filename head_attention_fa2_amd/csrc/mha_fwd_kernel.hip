@@ -403,6 +403,8 @@ void mha_fwd_kernel(Params p) {
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) acc[dt] = f32x16_t{};
   float m_run = -__builtin_inff();   // exponent offset in raw score units
+  float mc = 0.f;                    // m_run * c2 once set
+  float thr = -__builtin_inff();     // m_run + kRescaleLog2 / c2
   float l_run = 0.f;                 // this lane's share of the row sum
   const float c2 = p.scale2;
 
@@ -464,34 +466,47 @@ void mha_fwd_kernel(Params p) {
           if (key > lim) s[ks][r] = -__builtin_inff();
         }
     }
-    // Online softmax (running max / sum of the "Long Softmax" puzzle).
-    float mx = s[0][0];
+    // Online softmax (running max / sum of the "Long Softmax" puzzle).  The tile's row
+    // max: three-way maxima in a tree, then the exchange between the two lane halves.
+    float part[kSlabs][6];
 #pragma unroll
-    for (int ks = 0; ks < kSlabs; ++ks)
+    for (int ks = 0; ks < kSlabs; ++ks) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ks][r]);
-    mx = max_halves(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const bool grow = (m_new - m_run) * c2 > kRescaleLog2;     // true on the first tile
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * c2);    // 0 when m_run = -inf
+      for (int g = 0; g < 5; ++g) part[ks][g] = fmaxf(fmaxf(s[ks][3 * g], s[ks][3 * g + 1]), s[ks][3 * g + 2]);
+      part[ks][5] = s[ks][15];
+    }
+    float mx = fmaxf(fmaxf(part[0][0], part[0][1]), part[0][5]);
+    float my = fmaxf(fmaxf(part[0][2], part[0][3]), part[0][4]);
+#pragma unroll
+    for (int ks = 1; ks < kSlabs; ++ks) {
+      mx = fmaxf(fmaxf(mx, part[ks][0]), fmaxf(part[ks][1], part[ks][5]));
+      my = fmaxf(fmaxf(my, part[ks][2]), fmaxf(part[ks][3], part[ks][4]));
+    }
+    mx = max_halves(fmaxf(mx, my));
+    // The offset moves only when the row max passes thr = offset + 2^8 in the exponent;
+    // always on the first tile (thr = -inf), whose row max is finite: the first tile of a
+    // row always holds a visible key.
+    if (__builtin_amdgcn_ballot_w64(mx > thr)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2((m_run - m_new) * c2);    // 0 when m_run = -inf
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) acc[dt] *= alpha;
-      m_run = m_use;
+      m_run = m_new;
+      mc = m_new * c2;
+      thr = m_new + kRescaleLog2 / c2;
     }
-    const float mc = (m_run == -__builtin_inff() ? 0.f : m_run) * c2;
-    float lsum = 0.f;
+    float la = 0.f, lb = 0.f;   // two partial sums: half the dependent-add chain
 #pragma unroll
     for (int ks = 0; ks < kSlabs; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = fast_exp2(__builtin_fmaf(s[ks][r], c2, -mc));
         s[ks][r] = e;
-        lsum += e;
+        if (r & 1) lb += e;
+        else la += e;
       }
-    l_run += lsum;
+    l_run += la + lb;
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
@@ -606,7 +621,7 @@ void mha_fwd_kernel(Params p) {
           const int col = k16 ? dt * 32 + 16 * (g >> 1) + 8 * G + 4 * (g & 1) : dt * 32 + 8 * g + 4 * G;
           *(f32x4_t*)(orow + col) = ov;
         }
-      if (G == 0) p.part_lse[r] = (m_run * c2 + __builtin_amdgcn_logf(l)) * kLn2;
+      if (G == 0) p.part_lse[r] = (mc + __builtin_amdgcn_logf(l)) * kLn2;
     }
     return;
   }
@@ -635,7 +650,7 @@ void mha_fwd_kernel(Params p) {
           *(f32x4_t*)(orow + dt * 32 + 8 * g + 4 * G) = ov;
         }
     }
-    if (G == 0) p.lse[(size_t)bh * N + qrow] = (m_run * c2 + __builtin_amdgcn_logf(l)) * kLn2;
+    if (G == 0) p.lse[(size_t)bh * N + qrow] = (mc + __builtin_amdgcn_logf(l)) * kLn2;
   }
 }
 
