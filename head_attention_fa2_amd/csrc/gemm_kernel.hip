@@ -81,16 +81,20 @@ struct Mfma<_Float16> {
 };
 
 // Tile configurations: a workgroup owns a BM x BN block of C with WM x WN wavefronts,
-// each accumulating (BM/WM) x (BN/WN) in 32 x 32 MFMA blocks; k-steps of 64.
-template <int BM_, int BN_, int WM_, int WN_>
+// each accumulating (BM/WM) x (BN/WN) in 32 x 32 MFMA blocks; k-steps of 64.  KG > 1:
+// KG groups of WM x WN wavefronts, each summing its own contiguous share of the k-steps
+// through its own LDS stages; the groups' sums are added through LDS at the end (a split
+// of K inside the workgroup: no workspace, C still rounded once).
+template <int BM_, int BN_, int WM_, int WN_, int KG_ = 1>
 struct Tiling {
-  static constexpr int BM = BM_, BN = BN_, BK = 64;
-  static constexpr int WM = WM_, WN = WN_, Waves = WM * WN, Threads = 64 * Waves;
+  static constexpr int BM = BM_, BN = BN_, BK = 64, KG = KG_;
+  static constexpr int WM = WM_, WN = WN_, Waves = WM * WN, Threads = 64 * Waves * KG;
   static constexpr int MB = BM / WM / 32, NB = BN / WN / 32;   // 32x32 blocks per wavefront
   static constexpr int RB = BN / 8;                           // 16-byte chunks per B row
   static constexpr int ATile = BM * BK * 2, BTile = BK * BN * 2, Stage = ATile + BTile;
-  static constexpr int LoadsA = ATile / 16 / Threads, LoadsB = BTile / 16 / Threads;
-  static_assert(LoadsA * 16 * Threads == ATile && LoadsB * 16 * Threads == BTile, "even split");
+  static constexpr int LoadsA = ATile / 16 / (64 * Waves), LoadsB = BTile / 16 / (64 * Waves);
+  static_assert(LoadsA * 16 * 64 * Waves == ATile && LoadsB * 16 * 64 * Waves == BTile, "even split");
+  static_assert(KG == 1 || 2 * Stage >= Waves * (BM / WM) * (BN / WN) * 4, "group sums fit its stages");
   static_assert(MB >= 1 && NB >= 1 && (RB == 8 || RB == 16 || RB == 32), "supported shapes");
 };
 // 256 x 256, 8 wavefronts of 128 x 64, one workgroup per CU (128 KiB of LDS).
@@ -100,14 +104,22 @@ typedef Tiling<256, 256, 2, 4> Large;
 typedef Tiling<128, 128, 2, 2> Small;
 // 128 x 64, 4 wavefronts of 64 x 32, three workgroups per CU (48 KiB of LDS each).
 typedef Tiling<128, 64, 2, 2> Tiny;
+// 128 x 128 with the k-steps split between two groups of 4 wavefronts of 64 x 64, one
+// workgroup of 8 wavefronts per CU (2 x 64 KiB of LDS): the 128 x 128 blocks' operand
+// reuse for grids too small to fill the CUs with 128 x 128 tiles.
+typedef Tiling<128, 128, 2, 2, 2> Duo;
 constexpr int kGroupM = 8;                 // block-rows per group of the tile order
 // Below this many 256 x 256 tiles (3/4 of the 256 CUs) the 128 x 128 tiling is used.
 // Measured on the Llama-3-8B shapes: 64 and 128 tiles run 1.2-1.7x faster as 128 x 128,
 // 224 tiles and more 1.2-1.3x slower.
 constexpr long kLargeMinTiles = 192;
 // Below this many 128 x 128 tiles (1.5 per CU) the 128 x 64 tiling is used: measured
-// 1.15-1.2x faster at 48-256 tiles, 1.5x slower at 512.
+// 1.15-1.2x faster at 48-256 tiles, 1.5x slower at 512 ...
 constexpr long kSmallMinTiles = 384;
+// ... unless K is at least this long: then the 128 x 128 tiling with the k-steps split
+// between two groups of wavefronts (measured at 256 tiles: 1.21x the 128 x 64 tiling at
+// K = 4096 and 1.28x at K = 14336; at K = 1000 it was 0.85x).
+constexpr int kDuoMinK = 2048;
 
 struct GemmParams {
   const void* a;
@@ -129,11 +141,15 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
   typedef typename Mfma<T>::v8 v8_t;
   constexpr int kBM = C::BM, kBN = C::BN, kBK = C::BK, kWaves = C::Waves, kWavesN = C::WN;
   constexpr int kMB = C::MB, kNB = C::NB, kATile = C::ATile, kStage = C::Stage;
-  constexpr int kLoadsA = C::LoadsA, kLoadsB = C::LoadsB, kRB = C::RB;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];   // [buf][A, B]
+  constexpr int kLoadsA = C::LoadsA, kLoadsB = C::LoadsB, kRB = C::RB, kKG = C::KG;
+  static_assert(!(SPLITK && kKG > 1), "split-K over workgroups uses one k-group");
+  __shared__ __attribute__((aligned(1024))) char lds[kKG * 2 * kStage];   // [group][buf][A, B]
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kgrp = wave_all / kWaves;             // k-group of this wavefront
+  const int wave = wave_all - kgrp * kWaves;      // wavefront within its group
+  char* const smem = lds + kgrp * 2 * kStage;     // this group's stages
   const int wave_m = wave / kWavesN, wave_n = wave % kWavesN;
   const int G = lane >> 5;
 
@@ -178,7 +194,19 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
     b_col[j] = (unsigned)min(n0 / 8 + c, N / 8 - 1) * 16u;
   }
   const int kend = SPLITK ? min(K, kbeg + p.kchunk) : K;
-  const int nk = (kend - kbeg + kBK - 1) / kBK;
+  int nk = (kend - kbeg + kBK - 1) / kBK;
+  int nsteps = nk;               // steps of the workgroup's loop (every group's barriers)
+  if constexpr (kKG > 1) {
+    // k-steps [0, h) for group 0, [h, nk) for group 1
+    const int h = (nk + 1) / 2;
+    nsteps = h;
+    if (kgrp == 1) {
+      kbeg = h * kBK;
+      nk -= h;
+    } else {
+      nk = h;
+    }
+  }
 
   // full k-steps: uniform (SGPR) bases advanced by k0 and per-lane offsets fixed for
   // the whole loop, so a copy costs no vector arithmetic
@@ -265,26 +293,30 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
     }
   };
 
+  // step t of the workgroup's loop; a k-group with fewer k-steps than the loop (the
+  // second group when their count is odd) only takes part in the barriers
   auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
+    const bool active = t < nk;
 #if MHA_SERIALIZE
     // race-check form: one buffer, copied, waited for and fenced before it is read
     constexpr int buf = 0;
     (void)buf_tag;
     tile_barrier();
-    issue(t, 0, kA | kB);
+    if (active) issue(t, 0, kA | kB);
 #else
     constexpr int buf = decltype(buf_tag)::value;
 #endif
     char* sa = smem + buf * kStage;
     wait_vmcnt<0>();
     const int k0 = kbeg + t * kBK;
-    if (k0 + kBK > K) {
+    if (active && k0 + kBK > K) {
       // ragged last k-step: zero the A chunks past K that this thread copied
 #pragma unroll
       for (int j = 0; j < kLoadsA; ++j)
         if (k0 + a_k[j] >= K) *(uint4*)(sa + (j * kWaves + wave) * 1024 + lane * 16) = uint4{0, 0, 0, 0};
     }
     tile_barrier();
+    if (!active) return;
 #if MHA_SERIALIZE
     compute(sa, sa + kATile, 0, kBK / 16);
 #else
@@ -299,11 +331,46 @@ __global__ __launch_bounds__(C::Threads) void gemm_kernel(GemmParams p) {
   };
 
 #if !MHA_SERIALIZE
-  issue(0, 0, kA | kB);
+  if (nk > 0) issue(0, 0, kA | kB);
 #endif
-  for (int t = 0; t < nk; t += 2) {
+  for (int t = 0; t < nsteps; t += 2) {
     step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < nk) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < nsteps) step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  if constexpr (kKG > 1) {
+    // group 1 hands its sums to group 0 through its own (now idle) stages: wavefront w
+    // of group 1 writes its accumulators lane-contiguously, wavefront w of group 0 (same
+    // block of C) adds them.  The barriers order the group's last operand reads before
+    // the writes, and the writes before the reads.
+    constexpr int kRegs = kMB * kNB * 16;
+    float* xfer = (float*)(lds + 2 * kStage) + (size_t)wave * kRegs * 64;
+    tile_barrier();
+    if (kgrp == 1) {
+#pragma unroll
+      for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4_t v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+            *(f32x4_t*)(xfer + (((i * kNB + j) * 4 + q) * 64 + lane) * 4) = v;
+          }
+    }
+    tile_barrier();
+    if (kgrp == 1) return;
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+      for (int j = 0; j < kNB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t v = *(const f32x4_t*)(xfer + (((i * kNB + j) * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
+        }
   }
 
   // --- epilogue: register r of block (i, j) is row (lane & 31) of the block and
@@ -386,12 +453,13 @@ void launch_tiled(GemmParams p, int dtype, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_kernel<__bf16, C>), dim3(p.total), dim3(C::Threads), 0, stream, p);
 }
 
-// 0: the 256 x 256 tiling, 1: 128 x 128, 2: 128 x 64.
-int gemm_tiling(int M, int N) {
+// 0: the 256 x 256 tiling, 1: 128 x 128, 2: 128 x 64, 3: 128 x 128 with two k-groups.
+int gemm_tiling(int M, int N, int K) {
   const long large = (long)((M + Large::BM - 1) / Large::BM) * ((N + Large::BN - 1) / Large::BN);
   if (large >= kLargeMinTiles) return 0;
   const long small = (long)((M + Small::BM - 1) / Small::BM) * ((N + Small::BN - 1) / Small::BN);
-  return small >= kSmallMinTiles ? 1 : 2;
+  if (small >= kSmallMinTiles) return 1;
+  return K >= kDuoMinK ? 3 : 2;
 }
 
 }  // namespace
@@ -405,13 +473,15 @@ hipError_t launch_gemm(const void* a, const void* b, void* c, int M, int N, int 
   p.M = M;
   p.N = N;
   p.K = K;
-  const int tiling = gemm_tiling(M, N);
+  const int tiling = gemm_tiling(M, N, K);
   if (tiling == 0)
     launch_tiled<Large>(p, dtype, stream);
   else if (tiling == 1)
     launch_tiled<Small>(p, dtype, stream);
-  else
+  else if (tiling == 2)
     launch_tiled<Tiny>(p, dtype, stream);
+  else
+    launch_tiled<Duo>(p, dtype, stream);
   return hipGetLastError();
 }
 

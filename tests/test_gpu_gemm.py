@@ -2,8 +2,9 @@
 CPU oracle's float64 product, within the oracle's bound for a float32-accumulated,
 once-rounded result (u_out |C| + gamma_K |A||B|, bf16 u = 2^-8, fp16 u = 2^-11).  The
 element-wise shapes cover ragged M, N and K (partial tiles, K not a multiple of the
-64-wide k-step) under the three tilings (256 x 256 from 192 such tiles, else 128 x 128
-from 384 such tiles, else 128 x 64); the full-size workloads are checked on sampled rows
+64-wide k-step) under the four tilings (256 x 256 from 192 such tiles, else 128 x 128
+from 384 such tiles, else for K >= 2048 128 x 128 with the k-steps split between two
+groups of wavefronts, else 128 x 64); the full-size workloads are checked on sampled rows
 and columns."""
 import numpy as np
 import pytest
@@ -43,6 +44,9 @@ CASES = [
     (4000, 3080, 1000, "bf16"), (3900, 3336, 264, "f16"),
     # 384-400 tiles of 128 x 128 (and under 192 large ones): the 128 x 128 tiling
     (2048, 3072, 264, "bf16"), (2000, 3080, 136, "f16"),
+    # fewer than 384 tiles of 128 x 128 and K >= 2048: two k-groups per workgroup, with an
+    # even, an odd and a ragged number of k-steps (the second group then has one fewer)
+    (130, 4104, 2048, "bf16"), (1000, 1032, 2056, "f16"), (700, 520, 2112, "bf16"), (1024, 1024, 4160, "bf16"),
 ]
 
 
@@ -61,6 +65,10 @@ def test_gemm_closed_forms():
     a_bits, _ = mha_inputs.draw_gemm(300, 8, 264, "bf16", seed=5)
     eye = mha_inputs.f32_to_bf16_bits(np.eye(264, dtype=np.float32))
     np.testing.assert_array_equal(_run(a_bits, eye, "bf16"), oracle.decode(a_bits, "bf16"))
+    # the same with K long enough for two k-groups (each sums 2048 ones exactly)
+    c = _run(mha_inputs.f32_to_bf16_bits(np.ones((200, 4096), np.float32)),
+             mha_inputs.f32_to_bf16_bits(np.ones((4096, 136), np.float32)), "bf16")
+    assert np.all(c == 4096.0)
 
 
 def test_gemm_scaled_operands():
