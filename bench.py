@@ -470,7 +470,7 @@ def main():
     del r, oracle_heads
     if args.sweep:
         for name, ww in mha_inputs.WORKLOADS.items():
-            rr = time_gpu(ww, max(5, args.steps // 2), 3, dev)
+            rr = time_gpu(ww, max(5, args.steps // 2), 3, dev, settle_s=0.5)
             m = rr["total_ms"] / max(5, args.steps // 2)
             tf = ww.credited_flops() / (m * 1e-3) / 1e12
             print(json.dumps({"workload": name, "ms": round(m, 5), "TFLOP/s": round(tf, 2),
@@ -537,7 +537,9 @@ def main():
     if args.pages_sweep:
         for name, ww in mha_inputs.SWEEP.items():
             steps = max(5, args.steps // 4)
-            rr = time_gpu(ww, steps, 5, dev)
+            # each shape settles the clock at its own load first: a long shape before a
+            # short one leaves the clock where the short one would not hold it
+            rr = time_gpu(ww, steps, 5, dev, settle_s=0.5)
             m = rr["total_ms"] / steps
             tf = ww.credited_flops() / (m * 1e-3) / 1e12
             print(json.dumps({"workload": name, "B": ww.B, "H": ww.H, "N": ww.N, "d": ww.d,

@@ -109,7 +109,7 @@ constexpr int kBM = kQW * kWaves;        // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;     // lazy-rescale threshold, in log2 units
-constexpr int kOrderHeads = 8;           // causal: heads per ordering group on an XCD
+constexpr int kOrderHeads = 4;           // causal: heads per ordering group on an XCD
 
 struct Params {
   const void* q;

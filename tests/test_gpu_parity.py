@@ -176,10 +176,11 @@ def test_out_buffers_fully_overwritten():
 
 
 # Causal launches with B*H a multiple of 8 take the grouped dispatch order (each XCD owns
-# B*H/8 whole heads, run in groups of eight, heaviest query blocks of a group first).
+# B*H/8 whole heads, run in groups of four, heaviest query blocks of a group first).
 # Element-wise against the oracle with 1, 2, 3, 5, 9, 16 and 17 heads per XCD (one
-# partial group for 3 and 5; a full group and a partial one for 9; two full groups for
-# 16; two full groups and a partial one for 17) and ragged query blocks.
+# partial group for 3; a full group and a partial one for 5; two full groups and a
+# partial one for 9; four full groups for 16, four and a partial one for 17) and ragged
+# query blocks.
 GROUPED = [(1, 8, 300, 64, "bf16"), (2, 8, 260, 128, "bf16"), (3, 8, 200, 64, "f16"),
            (5, 8, 257, 128, "bf16"), (1, 72, 130, 128, "f16"), (1, 8, 100, 128, "bf16"), (2, 4, 1, 64, "f16"),
            (2, 64, 140, 64, "bf16"), (1, 136, 129, 128, "f16")]
