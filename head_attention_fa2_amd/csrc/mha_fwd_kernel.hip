@@ -178,10 +178,26 @@ using gfx950::wait_vmcnt;
 // double-buffered 64-key tiles fit twice in the 160 KiB of LDS, else one (fp32 with
 // d = 128 needs 128 KiB).  Kernels that need fewer registers may run more (d = 64 on
 // 16-bit inputs: four).
-template <typename T, int D, bool SPLIT>
+template <typename T, int D, bool SPLIT, bool KSPLIT = false>
 constexpr int min_waves_per_eu() {
   constexpr int keys = tile_keys<T, D, SPLIT>();
+  if constexpr (KSPLIT) return D == 64 ? 4 : 2;   // 8-wavefront workgroups: up to two per CU at d = 64, one at d = 128
   return keys == 32 ? 3 : 2 * 2 * keys * D * (int)sizeof(T) <= 80 * 1024 ? 2 : 1;
+}
+
+// KSPLIT (fused forward on 16-bit inputs, for grids too small to fill the CUs): a workgroup
+// of 8 wavefronts in two groups of 4; both groups own the same 128 query rows, group 0
+// streams the first half of the key tiles and group 1 the second, each through its own
+// double-buffered LDS tiles, and group 1 hands its (O, l, offset) to group 0 through LDS
+// at the end, where they are merged exactly as two key ranges of the online softmax are:
+// offset m = max(m0, m1), O = O0 2^(c(m0-m)) + O1 2^(c(m1-m)), l likewise.
+template <typename T, int D, bool SPLIT, bool KSPLIT>
+constexpr int lds_bytes() {
+  constexpr int tile = tile_keys<T, D, SPLIT>() * D * (int)sizeof(T);
+  if constexpr (!KSPLIT) return 2 * 2 * tile;
+  constexpr int stages = 2 * 2 * 2 * tile;                       // [group][buf][K,V]
+  constexpr int merge = kWaves * ((D / 32) * 16 + 2) * 64 * 4;   // group 1's O, offset, l
+  return stages > merge ? stages : merge;
 }
 
 // SPLIT: the split-KV form (no mask): workgroup (split, head, query block) covers the
@@ -189,11 +205,13 @@ constexpr int min_waves_per_eu() {
 // own l) and logsumexp to the float32 partial buffers; mha_merge_kernel combines them.
 // PAGED (with SPLIT): K and V are gathered from block pools [num_blocks][H][bs][d]
 // through the block table; head b*H + h uses keys [0, seq_lens[b]).
-template <typename T, int D, bool CAUSAL, bool SPLIT = false, bool PAGED = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<T, D, SPLIT>())))
+template <typename T, int D, bool CAUSAL, bool SPLIT = false, bool PAGED = false, bool KSPLIT = false>
+__global__ __launch_bounds__(KSPLIT ? 2 * kThreads : kThreads)
+__attribute__((amdgpu_waves_per_eu(min_waves_per_eu<T, D, SPLIT, KSPLIT>())))
 void mha_fwd_kernel(Params p) {
   static_assert(!(SPLIT && CAUSAL), "the split-KV form has no mask");
   static_assert(!PAGED || SPLIT, "paged K/V uses the split-KV form");
+  static_assert(!KSPLIT || (!SPLIT && sizeof(T) == 2), "key halves per workgroup: fused forward, 16-bit");
   constexpr int kBN = tile_keys<T, D, SPLIT>();  // keys per K/V tile
   constexpr int kSlabs = kBN / 32;               // 32-key MFMA slabs per tile
   constexpr bool k16 = sizeof(T) == 2;         // bf16 or fp16 inputs
@@ -203,12 +221,16 @@ void mha_fwd_kernel(Params p) {
   constexpr int kTileBytes = kBN * RB;
   constexpr int kLoads = kBN * R / kThreads;     // 16-byte loads per thread per tile
   static_assert(kLoads * kThreads == kBN * R, "tile must split evenly");
+  static_assert(lds_bytes<T, D, SPLIT, KSPLIT>() >= (KSPLIT ? 2 : 1) * 2 * 2 * kTileBytes, "LDS stages");
   constexpr int kDT = D / 32;                    // 32-wide output column blocks
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTileBytes];  // [buf][K,V]
+  __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<T, D, SPLIT, KSPLIT>()];  // [group][buf][K,V]
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kgrp = KSPLIT ? wave_all >> 2 : 0;  // key half of this wavefront (KSPLIT)
+  const int wave = wave_all - kgrp * kWaves;    // wavefront within its group: its query rows
+  char* const smem = lds + kgrp * 2 * 2 * kTileBytes;
   const int n = lane & 31;      // query column (and K row slot) within the wavefront
   const int G = lane >> 5;      // lane half
 
@@ -252,7 +274,7 @@ void mha_fwd_kernel(Params p) {
     head_h = bh - seq_b * p.H;
     Nk = min(max(p.seq_lens[seq_b], 0), p.max_blocks << p.bs_log2);
   }
-  const int kbeg = SPLIT ? split * p.chunk : 0; // this workgroup's keys: [kbeg, kend)
+  int kbeg = SPLIT ? split * p.chunk : 0;       // this workgroup's keys: [kbeg, kend)
   const int kend = SPLIT ? min(Nk, kbeg + p.chunk) : N;
   const int q0 = qb * kBM;
   const int qw = q0 + wave * kQW;               // first query row of this wavefront
@@ -264,7 +286,19 @@ void mha_fwd_kernel(Params p) {
   const char* Vbase = (const char*)((const T*)p.v + khead);
 
   const int kv_end = CAUSAL ? min(N, q0 + kBM) : kend;
-  const int ntiles = PAGED ? max(0, (kv_end - kbeg + kBN - 1) / kBN) : (kv_end - kbeg + kBN - 1) / kBN;
+  int ntiles = PAGED ? max(0, (kv_end - kbeg + kBN - 1) / kBN) : (kv_end - kbeg + kBN - 1) / kBN;
+  int nsteps = ntiles;                          // steps of the loop (every wavefront's barriers)
+  if constexpr (KSPLIT) {
+    // group 0: tiles [0, h), group 1: tiles [h, ntiles)
+    const int h = (ntiles + 1) / 2;
+    nsteps = h;
+    if (kgrp == 1) {
+      kbeg = h * kBN;
+      ntiles -= h;
+    } else {
+      ntiles = h;
+    }
+  }
   // paged: a key range that starts past this sequence's end has nothing to do; the merge
   // reads only the ranges below the sequence's key count
   if (PAGED && ntiles == 0) return;
@@ -570,7 +604,7 @@ void mha_fwd_kernel(Params p) {
     (void)buf_tag;
     tile_barrier();                                    // every wavefront is done with tile t-1
     if constexpr (PAGED) fetch_entries(t);
-    issue_tile(t, 0);
+    if (!KSPLIT || t < ntiles) issue_tile(t, 0);
     wait_vmcnt<0>();
     tile_barrier();                                    // tile t has landed for every wavefront
 #else
@@ -583,6 +617,7 @@ void mha_fwd_kernel(Params p) {
     }
 #endif
     const int k0 = kbeg + t * kBN;
+    if (KSPLIT && t >= ntiles) return;                 // this key half has no tile t
     if (SPLIT && qw >= N) return;                      // no query row in this wavefront
     if (!CAUSAL || k0 <= qw + kQW - 1) {               // else: every key is after every row
       const bool need_mask = (k0 + kBN > kend) || (CAUSAL && k0 + kBN - 1 > qw);
@@ -591,14 +626,54 @@ void mha_fwd_kernel(Params p) {
   };
 #if !MHA_SERIALIZE
   if constexpr (PAGED) fetch_entries(0);
-  issue_tile(0, 0);
+  if (!KSPLIT || ntiles > 0) issue_tile(0, 0);
   if constexpr (PAGED) {
     if (ntiles > 1) fetch_entries(1);
   }
 #endif
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = 0; t < nsteps; t += 2) {
     step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < nsteps) step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  if constexpr (KSPLIT) {
+    // group 1 hands its state to group 0 (same wavefront slot: same query rows, and lane
+    // for lane the same half of each row).  The barriers order every wavefront's last
+    // tile reads before the writes, and the writes before the reads.
+    constexpr int kRegs = kDT * 16;
+    float* const xf = (float*)lds + (size_t)wave * (kRegs + 2) * 64;
+    tile_barrier();
+    if (kgrp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[dt][4 * q + e];
+          *(f32x4_t*)(xf + ((dt * 4 + q) * 64 + lane) * 4) = v;
+        }
+      xf[kRegs * 64 + lane] = m_run;          // -inf when this half had no tile for the row
+      xf[kRegs * 64 + 64 + lane] = l_run;
+    }
+    tile_barrier();
+    if (kgrp == 1) return;
+    const float m1 = xf[kRegs * 64 + lane];
+    const float l1 = xf[kRegs * 64 + 64 + lane];
+    const float mn = fmaxf(m_run, m1);        // m_run is finite: group 0 always has tile 0
+    const float a0 = fast_exp2((m_run - mn) * c2);
+    const float a1 = fast_exp2((m1 - mn) * c2);   // 0 when m1 = -inf
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t v = *(const f32x4_t*)(xf + ((dt * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[dt][4 * q + e] = acc[dt][4 * q + e] * a0 + v[e] * a1;
+      }
+    l_run = l_run * a0 + l1 * a1;
+    m_run = mn;
+    mc = mn * c2;
   }
 
   // --- epilogue: O = acc / l, lse = m + ln l, each written once.
@@ -658,6 +733,22 @@ template <typename T, int D, bool CAUSAL>
 hipError_t launch(const Params& p, hipStream_t stream) {
   hipLaunchKernelGGL((mha_fwd_kernel<T, D, CAUSAL>), dim3(p.total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+// 16-bit inputs: grids of at most one workgroup per CU (256 CUs) with at least two key
+// tiles run the key-half form, which puts twice the wavefronts on each CU (measured on
+// 256-workgroup grids: 1.06-1.09x at d = 128, 1.15-1.23x causal).  Larger grids keep the
+// 4-wavefront form: at 512 workgroups and d = 64 (two per CU) the two forms were level
+// (0.99-1.01x), the merge costing what the extra wavefronts gain.
+template <typename T, int D, bool CAUSAL>
+hipError_t launch16(const Params& p, hipStream_t stream) {
+  constexpr int kCUs = 256;
+  if (p.total <= kCUs && p.N > tile_keys<T, D, false>()) {
+    hipLaunchKernelGGL((mha_fwd_kernel<T, D, CAUSAL, false, false, true>), dim3(p.total), dim3(2 * kThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+  }
+  return launch<T, D, CAUSAL>(p, stream);
 }
 
 // Merge of the split-KV partial results (the cross-partition reduction of split-KV
@@ -784,12 +875,12 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
   p.qmul = scale > 0.f ? 1.f : (scale < 0.f ? -1.f : 0.f);
   p.scale2 = (scale != 0.f ? fabsf(scale) : 1.f) * kLog2e;
   if (dtype == 1) {
-    if (d == 64) return causal ? launch<__bf16, 64, true>(p, stream) : launch<__bf16, 64, false>(p, stream);
-    return causal ? launch<__bf16, 128, true>(p, stream) : launch<__bf16, 128, false>(p, stream);
+    if (d == 64) return causal ? launch16<__bf16, 64, true>(p, stream) : launch16<__bf16, 64, false>(p, stream);
+    return causal ? launch16<__bf16, 128, true>(p, stream) : launch16<__bf16, 128, false>(p, stream);
   }
   if (dtype == 2) {
-    if (d == 64) return causal ? launch<_Float16, 64, true>(p, stream) : launch<_Float16, 64, false>(p, stream);
-    return causal ? launch<_Float16, 128, true>(p, stream) : launch<_Float16, 128, false>(p, stream);
+    if (d == 64) return causal ? launch16<_Float16, 64, true>(p, stream) : launch16<_Float16, 64, false>(p, stream);
+    return causal ? launch16<_Float16, 128, true>(p, stream) : launch16<_Float16, 128, false>(p, stream);
   }
   if (d == 64) return causal ? launch<float, 64, true>(p, stream) : launch<float, 64, false>(p, stream);
   return causal ? launch<float, 128, true>(p, stream) : launch<float, 128, false>(p, stream);

@@ -183,7 +183,7 @@ def test_out_buffers_fully_overwritten():
 # query blocks.
 GROUPED = [(1, 8, 300, 64, "bf16"), (2, 8, 260, 128, "bf16"), (3, 8, 200, 64, "f16"),
            (5, 8, 257, 128, "bf16"), (1, 72, 130, 128, "f16"), (1, 8, 100, 128, "bf16"), (2, 4, 1, 64, "f16"),
-           (2, 64, 140, 64, "bf16"), (1, 136, 129, 128, "f16")]
+           (2, 64, 140, 64, "bf16"), (1, 136, 129, 128, "f16"), (1, 264, 130, 64, "bf16")]
 
 
 @pytest.mark.parametrize("B,H,N,d,dtype", GROUPED)
@@ -193,6 +193,27 @@ def test_causal_grouped_order_elementwise(B, H, N, d, dtype):
     o, lse = gu.run(q, k, v, dtype, True, scale)
     o_ref, l_ref = gu.oracle_full(q, k, v, dtype, True, scale)
     _check(o, lse, o_ref, l_ref, dtype, f"grouped causal B{B} H{H} N{N} d{d} {dtype}")
+
+
+# 16-bit launches of at most 256 workgroups with more than one K/V tile run the key-half
+# form (8 wavefronts per workgroup, two halves of the key tiles merged at the end); larger
+# grids the 4-wavefront form.  Shapes on both sides of the threshold, causal and not,
+# with ragged query blocks.
+FORMS = [(1, 128, 256, 64, False, "bf16"), (1, 130, 256, 64, False, "bf16"),      # 256 | 260 workgroups
+         (1, 128, 256, 128, False, "f16"), (1, 130, 256, 128, False, "f16"),      # 256 | 260
+         (1, 64, 500, 64, True, "bf16"), (1, 66, 500, 64, True, "bf16"),          # 256 | 264
+         (1, 64, 510, 128, True, "bf16"), (1, 66, 510, 128, True, "f16"),         # 256 | 264
+         (1, 4, 65, 128, True, "bf16"), (3, 5, 33, 128, False, "bf16"),           # two tiles / ragged
+         (2, 3, 64, 64, False, "f16"), (2, 3, 65, 64, False, "f16")]              # one tile | two
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,dtype", FORMS)
+def test_both_kernel_forms_elementwise(B, H, N, d, causal, dtype):
+    q, k, v = gu.draw(B, H, N, d, dtype, seed=4000 + B * H + N + d)
+    scale = 1 / math.sqrt(d)
+    o, lse = gu.run(q, k, v, dtype, causal, scale)
+    o_ref, l_ref = gu.oracle_full(q, k, v, dtype, causal, scale)
+    _check(o, lse, o_ref, l_ref, dtype, f"forms B{B} H{H} N{N} d{d} causal={causal} {dtype}")
 
 
 @pytest.mark.parametrize("B,H,N,d", [(4, 32, 4096, 128), (1, 32, 16384, 128), (3, 40, 1000, 64)])

@@ -47,6 +47,8 @@ FWD = [
     ("bf16", 1, 8, 2049, 128, False),
     ("f16", 2, 4, 777, 64, True),
     ("f16", 1, 4, 1100, 128, False),
+    ("bf16", 1, 130, 256, 64, False),   # grids above the key-half threshold: 4-wavefront form
+    ("f16", 1, 130, 300, 128, True),
     ("f32", 1, 2, 300, 64, False),
     ("f32", 1, 2, 200, 128, True),
 ]
