@@ -34,10 +34,11 @@
 //    K (ds_read_b128) and of V^T (ds_read_b64_tr_b16, the gfx950 transposing LDS read)
 //    are free of bank conflicts.
 //  * exp is evaluated as exp2 with the scale folded into one FMA (log2(e) prescale, as
-//    the "Long Softmax" puzzle recommends).  The output rescale is lazy: the running max
-//    used as exponent offset is only moved when the true max exceeds it by more than
-//    2^8 in the exponent, so O and l are rarely rescaled; the final O / l and
-//    m + ln l are exact for whichever offset was used.
+//    the "Long Softmax" puzzle recommends).  The exponent offset is lazy: it is set to
+//    the row max on a wavefront's first tile and afterwards only moved when a tile's
+//    exponentials grow large (a lane's sum of them above 2^24, or 2^15 for fp16), so
+//    most tiles take no row max at all and O and l are rarely rescaled; the final O / l
+//    and m + ln l are exact for whichever offset was used.
 //  * Causal: key tiles entirely above a wavefront's rows are skipped, only tiles that
 //    cross the diagonal (or the ragged end of the sequence) evaluate the mask, and
 //    heavy (late) query blocks are dispatched first.  Workgroup ids are
@@ -108,7 +109,13 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBM = kQW * kWaves;        // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleLog2 = 8.0f;     // lazy-rescale threshold, in log2 units
+// Lazy offset: a tile's exponentials are taken against the current offset, and the
+// offset is only moved (the tile's scores formed again and its row max taken) when some
+// lane's sum of them exceeds this bound, so every exponential used is at most the bound:
+// 2^24 (O and l then stay far from the float32 range for any sequence length and any
+// |v| below 2^80), and 2^15 when P is rounded to float16, whose largest value is 65504.
+template <typename T>
+constexpr float sum_limit() { return std::is_same<T, _Float16>::value ? 32768.0f : 16777216.0f; }
 constexpr int kOrderHeads = 4;           // causal: heads per ordering group on an XCD
 
 struct Params {
@@ -438,18 +445,20 @@ void mha_fwd_kernel(Params p) {
   for (int dt = 0; dt < kDT; ++dt) acc[dt] = f32x16_t{};
   float m_run = -__builtin_inff();   // exponent offset in raw score units
   float mc = 0.f;                    // m_run * c2 once set
-  float thr = -__builtin_inff();     // m_run + kRescaleLog2 / c2
   float l_run = 0.f;                 // this lane's share of the row sum
+  bool fresh = true;                 // no tile consumed yet: the offset is unset
   const float c2 = p.scale2;
 
-  auto compute_tile = [&](const char* lk, const char* lv, int k0, bool masked) __attribute__((always_inline)) {
-    // S^T = K_j . Q^T : one or two 32-key slabs, accumulated in alternation so consecutive
-    // MFMAs are independent; K operands are read two steps ahead.  With two slabs the
-    // wavefront raises its issue priority for these MFMAs, as for P.V below; a single slab
-    // is one dependent MFMA chain, and raising the priority there only holds back the
-    // other wavefronts' softmax while the chain waits on itself (measured +1-2 % at d = 128
+  // S^T = K_j . Q^T for the tile at lk (keys k0..), masked when `masked`.
+  auto scores = [&](f32x16_t (&s)[kSlabs], const char* lk, int k0, bool masked) __attribute__((always_inline)) {
+    // One or two 32-key slabs, accumulated in alternation so consecutive MFMAs are
+    // independent; K operands are read two steps ahead.  With two slabs the wavefront
+    // raises its issue priority for these MFMAs, as for P.V below; a single slab is one
+    // dependent MFMA chain, and raising the priority there only holds back the other
+    // wavefronts' softmax while the chain waits on itself (measured +1-2 % at d = 128
     // without it).
-    f32x16_t s[kSlabs] = {};
+#pragma unroll
+    for (int ks = 0; ks < kSlabs; ++ks) s[ks] = f32x16_t{};
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kSlabs == 2) __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
@@ -500,8 +509,13 @@ void mha_fwd_kernel(Params p) {
           if (key > lim) s[ks][r] = -__builtin_inff();
         }
     }
-    // Online softmax (running max / sum of the "Long Softmax" puzzle).  The tile's row
-    // max: three-way maxima in a tree, then the exchange between the two lane halves.
+  };
+
+  // Online softmax (running max / sum of the "Long Softmax" puzzle), offset update: the
+  // tile's row max (three-way maxima in a tree, then the exchange between the two lane
+  // halves) becomes the offset if it is larger, and O and l are rescaled to it.  Every
+  // row has a visible key in a wavefront's first tile, so the offset is finite after it.
+  auto rebase = [&](const f32x16_t (&s)[kSlabs]) __attribute__((always_inline)) {
     float part[kSlabs][6];
 #pragma unroll
     for (int ks = 0; ks < kSlabs; ++ks) {
@@ -517,19 +531,17 @@ void mha_fwd_kernel(Params p) {
       my = fmaxf(fmaxf(my, part[ks][2]), fmaxf(part[ks][3], part[ks][4]));
     }
     mx = max_halves(fmaxf(mx, my));
-    // The offset moves only when the row max passes thr = offset + 2^8 in the exponent;
-    // always on the first tile (thr = -inf), whose row max is finite: the first tile of a
-    // row always holds a visible key.
-    if (__builtin_amdgcn_ballot_w64(mx > thr)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2((m_run - m_new) * c2);    // 0 when m_run = -inf
-      l_run *= alpha;
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2((m_run - m_new) * c2);    // 0 when m_run = -inf
+    l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) acc[dt] *= alpha;
-      m_run = m_new;
-      mc = m_new * c2;
-      thr = m_new + kRescaleLog2 / c2;
-    }
+    for (int dt = 0; dt < kDT; ++dt) acc[dt] *= alpha;
+    m_run = m_new;
+    mc = m_new * c2;
+  };
+
+  // P = exp2(c2 * s - offset) in place; returns this lane's sum of them.
+  auto exponentials = [&](f32x16_t (&s)[kSlabs]) __attribute__((always_inline)) {
     float la = 0.f, lb = 0.f;   // two partial sums: half the dependent-add chain
 #pragma unroll
     for (int ks = 0; ks < kSlabs; ++ks)
@@ -540,7 +552,27 @@ void mha_fwd_kernel(Params p) {
         if (r & 1) lb += e;
         else la += e;
       }
-    l_run += la + lb;
+    return la + lb;
+  };
+
+  auto compute_tile = [&](const char* lk, const char* lv, int k0, bool masked) __attribute__((always_inline)) {
+    f32x16_t s[kSlabs];
+    scores(s, lk, k0, masked);
+    if (fresh) {
+      rebase(s);
+      fresh = false;
+    }
+    // The offset stays put while the exponentials stay small: no row max on such tiles.
+    // A lane sum above sum_limit (a key far above the offset; inf on overflow) sends the
+    // whole wavefront back to form the tile's scores again from the LDS tile, move the
+    // offset to the row max and exponentiate again (every value then at most 1).
+    float ls = exponentials(s);
+    if (__builtin_amdgcn_ballot_w64(ls > sum_limit<T>())) {
+      scores(s, lk, k0, masked);
+      rebase(s);
+      ls = exponentials(s);
+    }
+    l_run += ls;
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);

@@ -120,6 +120,32 @@ def test_scales_and_large_logits(dtype):
             _check(o, lse, o_ref, l_ref, dtype, f"sigma={sigma} scale={scale} causal={causal}", mag)
 
 
+# Rows whose maximum keeps climbing: key norms ramp up along the sequence, Q has a
+# positive mean, and a few keys are spikes along that mean, so that some logits jump far
+# above every earlier one (up to ~200, where exp of the old offset overflows float32).
+# The kernel's exponent offset must move on such tiles (the scores re-formed, the row
+# max taken, O and l rescaled); in both kernel forms (small and large grids).
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", [(1, 2, 700), (1, 90, 300)])
+def test_offset_moves_elementwise(dtype, d, B, H, N):
+    rng = np.random.default_rng(7000 + d + N)
+    q = rng.standard_normal((B, H, N, d)).astype(np.float32) + 0.5
+    k = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    k *= (1.0 + 3.0 * np.arange(N) / N).astype(np.float32)[None, None, :, None]
+    scale = 1 / math.sqrt(d)
+    for j, logit in ((N // 5, 20.0), (N // 3, 60.0), (2 * N // 3, 200.0), (N - 1, 30.0)):
+        k[:, :, j, :] = logit / (0.5 * d * scale)      # q.k * scale ~ logit on average
+    v = rng.uniform(-1.0, 1.0, (B, H, N, d)).astype(np.float32)
+    enc = {"bf16": mha_inputs.f32_to_bf16_bits, "f16": mha_inputs.f32_to_f16_bits, "f32": lambda a: a}[dtype]
+    q, k, v = enc(q), enc(k), enc(v)
+    for causal in (False, True):
+        o, lse = gu.run(q, k, v, dtype, causal, scale)
+        o_ref, l_ref = gu.oracle_full(q, k, v, dtype, causal, scale)
+        mag = max(1.0, float(np.max(np.abs(l_ref))) / 16.0) if dtype == "f32" else 1.0
+        _check(o, lse, o_ref, l_ref, dtype, f"offset moves {dtype} d{d} B{B} H{H} N{N} causal={causal}", mag)
+
+
 # ---------------------------------------------------------------- invariants on GPU output
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
