@@ -389,9 +389,10 @@ void mha_fwd_kernel(Params p) {
       }
     } else {
       // ragged last tile: rows past the end re-read the last key (finite, masked later)
+      const int last = kend - 1 - k0;   // (uniform: no per-tile update of per-lane rows)
 #pragma unroll
       for (int j = 0; j < kLoads; ++j) {
-        const int row = min(k0 + ld_row[j], kend - 1) - k0;
+        const int row = min(ld_row[j], last);
         const unsigned off = (unsigned)(row * RB + ld_chunk[j] * 16);
         const int dst = (j * kWaves + wave) * 1024;
         copy_to_lds(kg, off, lds_addr(lk + dst));
@@ -501,13 +502,12 @@ void mha_fwd_kernel(Params p) {
     // k0 + 32ks + 16(r>>3) + 8G + (r&7).
     if (masked) {
       const int lim = CAUSAL ? min(qrow, N - 1) : kend - 1;
+      const int rel = lim - k0 - 8 * G;   // key > lim  <=>  32ks + 16(r>>3) + (r&7) > rel
 #pragma unroll
       for (int ks = 0; ks < kSlabs; ++ks)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * ks + 16 * (r >> 3) + 8 * G + (r & 7);
-          if (key > lim) s[ks][r] = -__builtin_inff();
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * ks + 16 * (r >> 3) + (r & 7) > rel) s[ks][r] = -__builtin_inff();
     }
   };
 
@@ -542,15 +542,15 @@ void mha_fwd_kernel(Params p) {
 
   // P = exp2(c2 * s - offset) in place; returns this lane's sum of them.
   auto exponentials = [&](f32x16_t (&s)[kSlabs]) __attribute__((always_inline)) {
-    float la = 0.f, lb = 0.f;   // two partial sums: half the dependent-add chain
+    float la, lb;   // two partial sums: half the dependent-add chain
 #pragma unroll
     for (int ks = 0; ks < kSlabs; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = fast_exp2(__builtin_fmaf(s[ks][r], c2, -mc));
         s[ks][r] = e;
-        if (r & 1) lb += e;
-        else la += e;
+        if (ks == 0 && r < 2) (r ? lb : la) = e;
+        else (r & 1 ? lb : la) += e;
       }
     return la + lb;
   };
