@@ -307,8 +307,17 @@ void mha_fwd_kernel(Params p) {
     }
   }
   // paged: a key range that starts past this sequence's end has nothing to do; the merge
-  // reads only the ranges below the sequence's key count
-  if (PAGED && ntiles == 0) return;
+  // reads only the ranges below the sequence's key count.  With a single range (no
+  // merge) an empty sequence's rows are written here: O = 0 and lse = log 0 = -inf.
+  if (PAGED && ntiles == 0) {
+    if (p.splits == 1 && qrow < N) {
+      T* orow = (T*)p.o + head + (size_t)qrow * D;
+#pragma unroll
+      for (int c = G * (D / 2); c < (G + 1) * (D / 2); c += 16 / (int)sizeof(T)) *(f32x4_t*)(orow + c) = f32x4_t{};
+      if (G == 0) p.lse[(size_t)bh * N + qrow] = -__builtin_inff();
+    }
+    return;
+  }
 
   // --- tile loader: thread (wave, lane) copies kLoads 16-byte chunks of K and of V.
   // Load j of a thread fills LDS bytes [(j*kWaves + wave)*1024, +1024); the swizzle is
@@ -711,8 +720,9 @@ void mha_fwd_kernel(Params p) {
   // --- epilogue: O = acc / l, lse = m + ln l, each written once.
   const float l = sum_halves(l_run);
   const float inv = 1.0f / l;
-  if constexpr (SPLIT) {
+  if (SPLIT && p.splits > 1) {
     // partial result of this key range: O_s = acc / l (float32) and lse_s = m + ln l
+    // (a single range is the whole result: written below as the fused form writes it)
     if (qrow < N) {
       const size_t r = ((size_t)split * p.BH + bh) * (size_t)N + qrow;
       float* orow = p.part_o + r * D;
@@ -787,30 +797,36 @@ hipError_t launch16(const Params& p, hipStream_t stream) {
 // decoding): for one query row with partials (O_s, lse_s), s = 0..S-1,
 //   lse = M + ln L,  M = max_s lse_s,  L = sum_s exp(lse_s - M),
 //   O   = sum_s w_s * O_s,  w_s = exp(lse_s - M) / L.
-// One workgroup of kMergeThreads per row: M and L are block reductions over the splits,
-// the weights go to LDS, then thread c forms column c.
+// One workgroup of kMergeThreads per row.  M and L are block reductions over the splits
+// (in-wavefront butterflies, then the 4 wavefront results through LDS); the weights go to
+// LDS.  For O the threads form kGroups groups of D/4: thread (g, c) reads 4 columns of
+// the partials s = g, g + kGroups, ... (16-byte loads, several in flight), and the
+// groups' sums are added through LDS.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeLdsWeights = 2048;
 
 __device__ __forceinline__ float block_reduce(float x, float* red, bool is_max) {
-  red[threadIdx.x] = x;
-  __syncthreads();
-  for (int off = kMergeThreads / 2; off > 0; off >>= 1) {
-    if ((int)threadIdx.x < off) {
-      const float y = red[threadIdx.x + off];
-      red[threadIdx.x] = is_max ? fmaxf(red[threadIdx.x], y) : red[threadIdx.x] + y;
-    }
-    __syncthreads();
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float y = __shfl_xor(x, off);
+    x = is_max ? fmaxf(x, y) : x + y;
   }
-  const float r = red[0];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  __syncthreads();   // red is written again by the next reduction
   return r;
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(kMergeThreads) void mha_merge_kernel(Params p) {
-  __shared__ float red[kMergeThreads];
+  constexpr int kCols = D / 4;                       // threads per partial row (4 columns each)
+  constexpr int kGroups = kMergeThreads / kCols;     // partial rows read side by side
+  __shared__ float red[kMergeThreads / 64];
   __shared__ float wts[kMergeLdsWeights];
+  __shared__ f32x4_t sums[kGroups][kCols];
   const size_t row = blockIdx.x;                      // (b*H + h) * N + query row
   const size_t stride = (size_t)p.BH * (size_t)p.N;   // between splits
   const int t = threadIdx.x;
@@ -836,16 +852,25 @@ __global__ __launch_bounds__(kMergeThreads) void mha_merge_kernel(Params p) {
     sum += e;
     if (s < kMergeLdsWeights) wts[s] = e;
   }
-  const float L = block_reduce(sum, red, false);     // also orders the wts writes
-  const float invL = 1.0f / L;
-  for (int c = t; c < D; c += kMergeThreads) {
-    float o = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float w = s < kMergeLdsWeights ? wts[s]
-                                           : __builtin_amdgcn_exp2f((p.part_lse[s * stride + row] - M) * kLog2e);
-      o += w * p.part_o[(s * stride + row) * D + c];
-    }
-    ((T*)p.o)[row * D + c] = (T)(o * invL);
+  const float L = block_reduce(sum, red, false);     // its barrier also orders the wts writes
+  const int c = t % kCols, g = t / kCols;
+  const float* po = p.part_o + row * D + 4 * c;
+  f32x4_t acc = {};
+#pragma unroll 4
+  for (int s = g; s < splits; s += kGroups) {
+    const float w = s < kMergeLdsWeights ? wts[s]
+                                         : __builtin_amdgcn_exp2f((p.part_lse[s * stride + row] - M) * kLog2e);
+    acc += w * *(const f32x4_t*)(po + (size_t)s * stride * D);
+  }
+  sums[g][c] = acc;
+  __syncthreads();
+  if (t < kCols) {
+    f32x4_t o = sums[0][t];
+#pragma unroll
+    for (int q = 1; q < kGroups; ++q) o += sums[q][t];
+    const float invL = 1.0f / L;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ((T*)p.o)[row * D + 4 * t + e] = (T)(o[e] * invL);
   }
   if (t == 0) p.lse[row] = M + __builtin_amdgcn_logf(L) * kLn2;
 }
@@ -854,7 +879,7 @@ template <typename T, int D, bool PAGED = false>
 hipError_t launch_split(const Params& p, hipStream_t stream) {
   hipLaunchKernelGGL((mha_fwd_kernel<T, D, false, true, PAGED>), dim3(p.total), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.splits == 1) return e;   // one range: the kernel wrote O and lse
   hipLaunchKernelGGL((mha_merge_kernel<T, D>), dim3(p.BH * p.N), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -75,6 +75,10 @@ CASES = [
     (2, 2, 130, 64, "bf16", 64, [1500, 64], 4),
     (1, 4, 1, 128, "f16", 16, [5000], 1000),
     (2, 2, 1, 128, "bf16", 1024, [3000, 2048], 0),
+    # one key range: the partial kernel writes O and lse itself (no merge), empty sequences too
+    (4, 2, 3, 128, "f16", 16, [0, 100, 0, 33], 1),
+    (3, 2, 2, 64, "f32", 64, [0, 500, 64], 1),
+    (2, 3, 1, 128, "bf16", 256, [700, 0], 1),
 ]
 
 
