@@ -112,8 +112,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Lazy offset: a tile's exponentials are taken against the current offset, and the
 // offset is only moved (the tile's scores formed again and its row max taken) when some
 // lane's sum of them exceeds this bound, so every exponential used is at most the bound:
-// 2^24 (O and l then stay far from the float32 range for any sequence length and any
-// |v| below 2^80), and 2^15 when P is rounded to float16, whose largest value is 65504.
+// 2^24 (the accumulated O then stays below Nk * 2^24 * max|v|, inside the float32 range
+// while Nk * max|v| < 2^100), and 2^15 when P is rounded to float16, whose largest value
+// is 65504.
 template <typename T>
 constexpr float sum_limit() { return std::is_same<T, _Float16>::value ? 32768.0f : 16777216.0f; }
 constexpr int kOrderHeads = 4;           // causal: heads per ordering group on an XCD
