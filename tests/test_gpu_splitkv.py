@@ -44,6 +44,7 @@ CASES = [
     (1, 2, 33, 700, 128, "f32", 3), (1, 1, 1, 2048, 64, "f32", 0), (2, 2, 130, 1500, 64, "bf16", 4),
     (1, 4, 1, 5000, 128, "f16", 1000), (3, 2, 1, 3000, 128, "bf16", 1), (1, 1, 200, 200, 128, "bf16", 2),
     (2, 2, 5, 900, 64, "f32", 1), (1, 3, 130, 777, 64, "f16", 1),      # one range: no merge
+    (1, 2, 1, 2100 * 64, 64, "bf16", 2100),   # more ranges than the merge keeps weights for in LDS
 ]
 
 
