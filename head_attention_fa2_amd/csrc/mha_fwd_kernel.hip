@@ -99,7 +99,7 @@ struct Half16<_Float16> {
 
 constexpr int kQW = 32;                  // query rows per wavefront
 // Keys per K/V tile: 32 for the fused kernel on 16-bit inputs with d = 128 (a 32 KiB
-// double-buffered tile set and 162 VGPRs let three workgroups share a CU; measured +1-4 %
+// double-buffered tile set and 160-165 VGPRs let three workgroups share a CU; measured +1-4 %
 // on d = 128 against 64-key tiles at two workgroups per CU, but -4 % at d = 64), 64
 // otherwise (split-KV and paged kernels included).
 template <typename T, int D, bool SPLIT>
