@@ -108,6 +108,54 @@ def time_gpu(w, steps, warmup, dev, settle_s=0.0):
     return dict(total_ms=total_ms, per_ms=per, wall_s=wall, settle=settle, inputs=(q, k, v), out=(o, lse))
 
 
+def time_vs_torch(w, passes, reps, dev):
+    """This library's forward and torch's fused attention (its flash backend only, so that
+    torch never takes its unfused math path) on the same device inputs, timed in
+    alternating passes after a clock settle; medians of the passes, in ms per launch.
+    None when torch has no flash kernel for the shape or element type."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    import head_attention_fa2_amd as mha
+    import mha_inputs
+
+    q, k, v = mha_inputs.draw_qkv(w)
+    tq, tk, tv = (_to_device(x, w.dtype, dev) for x in (q, k, v))
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def ours():
+        mha.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+
+    def theirs():
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            return F.scaled_dot_product_attention(tq, tk, tv, is_causal=w.causal, scale=w.scale)
+
+    try:
+        ref = theirs()
+        torch.cuda.synchronize(dev)
+    except RuntimeError as e:
+        return {"torch_flash": None, "reason": str(e).splitlines()[0][:160]}
+    settle_clock(lambda: (ours(), theirs()), dev, 1.0)
+    res = {"ours": [], "torch": []}
+    for _ in range(passes):
+        for key, f in (("ours", ours), ("torch", theirs)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                f()
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            res[key].append(e0.elapsed_time(e1) / reps)
+    ours()
+    torch.cuda.synchronize(dev)
+    diff = float((o.float() - ref.float()).abs().max())
+    med = {key: sorted(x)[len(x) // 2] for key, x in res.items()}
+    return {"ms": med["ours"], "torch_flash_ms": med["torch"], "max_abs_diff_O": diff}
+
+
 def settle_clock(call, dev, seconds):
     """Launch `call` back to back until `seconds` of wall time have passed (at least one
     launch), synchronising every few launches.  Under sustained load the MI355X lowers
@@ -396,6 +444,9 @@ def main():
                     help="also time the paged split-KV decode workloads (lines on stderr)")
     ap.add_argument("--pages-sweep", action="store_true",
                     help="also time the fp16 sweep of the paper's FlashAttention-2 figures (lines on stderr)")
+    ap.add_argument("--vs-torch", action="store_true",
+                    help="also time torch's fused attention (flash backend) beside this library on the "
+                         "16-bit workloads (lines on stderr)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 5 device-to-device copies of BYTES bytes (to scale HBM counters)")
     args = ap.parse_args()
@@ -547,6 +598,21 @@ def main():
                               "pct_of_peak": round(100 * tf / PEAK_TFLOPS[ww.dtype], 2),
                               "parity": parity_sample(ww, rr["inputs"], rr["out"], n=8)}),
                   file=sys.stderr, flush=True)
+            del rr
+    if args.vs_torch:
+        for name, ww in mha_inputs.WORKLOADS.items():
+            if ww.dtype == "f32":
+                continue
+            rr = time_vs_torch(ww, 5, max(5, args.steps // 10), dev)
+            out = {"workload": name}
+            if rr.get("ms"):
+                tf = ww.credited_flops() / (rr["ms"] * 1e-3) / 1e12
+                tft = ww.credited_flops() / (rr["torch_flash_ms"] * 1e-3) / 1e12
+                out.update({"TFLOP/s": round(tf, 1), "torch_flash_TFLOP/s": round(tft, 1),
+                            "vs_torch": round(tf / tft, 3), "max_abs_diff_O": rr["max_abs_diff_O"]})
+            else:
+                out.update(rr)
+            print(json.dumps(out), file=sys.stderr, flush=True)
             del rr
     print(json.dumps(line), flush=True)
 
