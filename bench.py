@@ -136,8 +136,8 @@ def time_vs_torch(w, passes, reps, dev):
     try:
         ref = theirs()
         torch.cuda.synchronize(dev)
-    except RuntimeError as e:
-        return {"torch_flash": None, "reason": str(e).splitlines()[0][:160]}
+    except (RuntimeError, NotImplementedError, ValueError) as e:   # no flash kernel for this case
+        return {"torch_flash": None, "reason": (str(e).splitlines() or [type(e).__name__])[0][:160]}
     settle_clock(lambda: (ours(), theirs()), dev, 1.0)
     res = {"ours": [], "torch": []}
     for _ in range(passes):
