@@ -135,7 +135,9 @@ double mha_fwd_bytes(int B, int H, int N, int d, mha_dtype dtype);
  *   other arguments as for mha_fwd.
  *
  * Errors as for mha_fwd, plus MHA_ERR_INVALID_ARG for Nq or Nk < 1, splits < 0, a null
- * workspace or one smaller than required.  Two kernels are enqueued on `stream`.
+ * workspace or one smaller than required.  The partial kernel and, with more than one
+ * range, the merge kernel are enqueued on `stream`; with a single range the partial
+ * kernel writes O and lse itself and the workspace is not written.
  */
 mha_status mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int Nq, int Nk, int d, float scale, mha_dtype dtype,
@@ -218,7 +220,8 @@ double mha_fwd_splitkv_bytes(int B, int H, int Nq, int Nk, int d, mha_dtype dtyp
  *   block_size  a power of two, 16 .. 65536 (else MHA_ERR_UNSUPPORTED)
  *   splits      key ranges per sequence over max_blocks * block_size keys; 0 =
  *               automatic (mha_fwd_paged_splits).  A range past a sequence's end
- *               costs one workgroup that exits at once.
+ *               costs one workgroup that exits at once.  With a single range no merge
+ *               is launched (as for mha_fwd_splitkv).
  *   workspace   as for mha_fwd_splitkv, of at least mha_fwd_paged_workspace_size(...)
  *               bytes.
  *   other arguments as for mha_fwd_splitkv.
